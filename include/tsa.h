@@ -1,0 +1,225 @@
+/*
+ * tsa.h -- top-k sparse decode attention over a paged KV cache, for AMD MI355X (gfx950).
+ *
+ * C ABI of libtsa.  Plain pointers and sizes only.  Every device pointer is memory the
+ * caller owns (for example a torch tensor's data_ptr()); the library owns only the opaque
+ * handles and their host-side metadata (free list, reference counts, LRU state).  It never
+ * allocates device memory on its own: sizes are queried up front and passed back in.
+ *
+ * Pages cited (the operations below restate what they define):
+ *   [paged-KV page]  "KV cache phân trang, hay vì sao đặt trước theo độ dài tối đa là hoang
+ *                    phí" (interactive-ebooks.coregenaihub.com, llm-moi/sinh-nhanh/kv-phan-trang)
+ *   [GLM5.3 page]    "Cơ chế chú ý thưa (Sparse Attention) trên GLM5.3 ảnh hưởng thế nào đến
+ *                    bộ nhớ HBM?" (aihot.vn)
+ *   [snapshot page]  hert4.github.io ai-infra-notes, "cat-it-di-nho-nhieu-hon"
+ *
+ * Conventions shared by every call:
+ *   - Status: every call returns a tsa_status; on failure tsa_last_error() holds a message
+ *     (per thread).  Argument and capacity errors are detected before any side effect: no
+ *     partial page allocation, nothing enqueued.  TSA_ERR_HIP reports a failed launch.
+ *   - Streams: device work is enqueued on the caller's stream (a hipStream_t passed as
+ *     void*; NULL = the default stream).  No call synchronizes the device.
+ *   - Handles are not thread-safe; distinct handles may be used from distinct threads.
+ *   - bf16 tensors are raw 16-bit bfloat16 values.  Layouts are row-major, innermost last.
+ *   - Token positions are logical positions inside one request.  Physical page ids appear
+ *     only inside page tables; the library translates (a write through an untranslated id
+ *     lands in the wrong slot without any error: [snapshot page], "Ba thứ chặn đường").
+ */
+#ifndef TSA_H
+#define TSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tsa_status {
+    TSA_OK = 0,
+    TSA_ERR_INVALID = -1,           /* bad pointer, shape, index or state */
+    TSA_ERR_OUT_OF_PAGES = -2,      /* the pool's free list cannot cover the request */
+    TSA_ERR_SHARED_PAGE_WRITE = -3, /* an append would write a page other tables also map */
+    TSA_ERR_HIP = -4,               /* a HIP runtime call or kernel launch failed */
+    TSA_ERR_CAPACITY = -5,          /* a caller-sized buffer (workspace, cache) is too small */
+    TSA_ERR_UNSUPPORTED = -6        /* a valid shape no kernel of this build handles */
+} tsa_status;
+
+/* Message for the last failure on this thread ("" if none).  Valid until the next call. */
+const char* tsa_last_error(void);
+
+/* Version of this ABI (incremented on any incompatible change). */
+int32_t tsa_abi_version(void);
+
+/* ------------------------------------------------------------------------------------
+ * KV pool: fixed-size pages in device memory.
+ * [paged-KV page], "Phân trang: bỏ luôn ràng buộc liền mạch": the pool is cut into pages of
+ * a fixed size and each request keeps a page table instead of one contiguous block.
+ *
+ * Device layouts (bf16), slot = page * page_size + position-in-page:
+ *   K   [num_layers][num_pages * page_size][num_kv_heads][head_dim_k]
+ *   V   [num_layers][num_pages * page_size][num_kv_heads][head_dim_v]   (absent if v_from_k)
+ *   IDX [num_layers][num_pages * page_size][index_dim]                   (absent if index_dim 0)
+ * With v_from_k = 1 the values are the first head_dim_v dims of each key row, as in the MQA
+ * mode of MLA where all query heads read one latent row ([GLM5.3 page], MLA-modes paragraph).
+ * ---------------------------------------------------------------------------------- */
+typedef struct tsa_pool_desc {
+    int32_t num_pages;     /* physical pages; > 0 */
+    int32_t page_size;     /* tokens per page; > 0 */
+    int32_t num_layers;    /* > 0 */
+    int32_t num_kv_heads;  /* > 0 */
+    int32_t head_dim_k;    /* multiple of 8, <= 1024 */
+    int32_t head_dim_v;    /* multiple of 8, <= head_dim_k when v_from_k */
+    int32_t v_from_k;      /* 0 or 1 */
+    int32_t index_dim;     /* indexer key width, multiple of 8, or 0 for no indexer */
+} tsa_pool_desc;
+
+typedef struct tsa_kv_pool tsa_kv_pool;
+
+/* Bytes the caller must allocate for each region (0 for an absent region).  The sizes are
+ * exact and explicit: nothing is over-reserved by a hidden multiple ([snapshot page], "Ba thứ
+ * chặn đường": a pool outside memory accounting asking for twice its size killed start-up). */
+tsa_status tsa_kv_pool_bytes(const tsa_pool_desc* desc, size_t* k_bytes, size_t* v_bytes,
+                             size_t* idx_bytes);
+
+/* Create a pool over caller-owned device memory.  k_dev / v_dev / idx_dev may all be NULL
+ * for a metadata-only pool (page tables, accounting; kernels then refuse it).  free_order
+ * (host, nullable = ascending ids) is a permutation of 0..num_pages-1: the order in which
+ * pages are handed out.  Allocation policy (the pages leave it open): requests are served in
+ * index order, each one's logical pages in order, popping from the front of free_order. */
+tsa_status tsa_kv_pool_create(const tsa_pool_desc* desc, void* k_dev, void* v_dev, void* idx_dev,
+                              const int32_t* free_order, tsa_kv_pool** out);
+tsa_status tsa_kv_pool_destroy(tsa_kv_pool* pool);
+
+/* Pages on the free list, and pages referenced by at least one table. */
+tsa_status tsa_kv_pool_usage(const tsa_kv_pool* pool, int32_t* free_pages, int32_t* used_pages);
+
+/* Reference count of physical page `page` (number of page-table entries pointing at it). */
+tsa_status tsa_kv_pool_refcount(const tsa_kv_pool* pool, int32_t page, int32_t* refcount);
+
+/* ------------------------------------------------------------------------------------
+ * Page tables (host arrays).
+ * [paged-KV page], "Phân trang": a request of length L holds ceil(L / page_size) pages.
+ * [paged-KV page], "Chia sẻ trang": requests sharing a prefix point at the same pages, but
+ * only the full pages of the prefix: the page holding the prefix end and the first differing
+ * token is private.  Saved pages = (members - 1) * floor(prefix / page_size).
+ *
+ * page_table: host int32 [n_req * max_pages], entry j of request i = physical page of its
+ * logical page j, -1 where unused.  num_pages: host int32 [n_req].
+ * ---------------------------------------------------------------------------------- */
+
+/* Allocate tables for n_req requests of lengths lens[i] (>= 0).  prefix_group (nullable):
+ * group id per request, -1 = none; prefix_len_of_group[g] (g < n_groups): prefix tokens of
+ * group g, <= every member's length.  A group's full prefix pages are taken when its first
+ * member (lowest index) is built; later members map the same pages (refcount = members).
+ * saved_pages (nullable) receives the pages sharing saved.  On TSA_ERR_OUT_OF_PAGES nothing
+ * is allocated. */
+tsa_status tsa_page_table_build(tsa_kv_pool* pool, int32_t n_req, const int32_t* lens,
+                                const int32_t* prefix_group, const int32_t* prefix_len_of_group,
+                                int32_t n_groups, int32_t max_pages, int32_t* page_table,
+                                int32_t* num_pages, int64_t* saved_pages);
+
+/* Extend tables so request i covers new_lens[i] tokens (no shrinking), popping new private
+ * pages in request order.  page_table / num_pages are updated in place; all-or-nothing. */
+tsa_status tsa_page_table_grow(tsa_kv_pool* pool, int32_t n_req, const int32_t* new_lens,
+                               int32_t max_pages, int32_t* page_table, int32_t* num_pages);
+
+/* Drop the tables' references; a page whose count reaches 0 returns to the free list
+ * (appended in table order).  Entries are not modified. */
+tsa_status tsa_page_table_release(tsa_kv_pool* pool, int32_t n_req, const int32_t* page_table,
+                                  const int32_t* num_pages, int32_t max_pages);
+
+/* ------------------------------------------------------------------------------------
+ * Appending tokens: scatter each new token's K, V and indexer key into the slot its page
+ * table assigns ([paged-KV page], "Phân trang": pages need not be contiguous; the table
+ * knows where each one is).
+ * ---------------------------------------------------------------------------------- */
+
+/* Host check for a planned append: every (req[i], pos[i]) must lie in an allocated page
+ * (pos < num_pages[req] * page_size) whose refcount is 1.  Returns TSA_ERR_SHARED_PAGE_WRITE
+ * for a shared page (copy-on-write is not provided), TSA_ERR_INVALID otherwise. */
+tsa_status tsa_kv_append_check(const tsa_kv_pool* pool, int32_t n_tok, const int32_t* req,
+                               const int32_t* pos, int32_t n_req, const int32_t* page_table,
+                               const int32_t* num_pages, int32_t max_pages);
+
+/* Device scatter of n_tok rows.  req_dev / pos_dev: device int32 [n_tok];
+ * page_table_dev: device int32 [n_req * max_pages].  k_src: bf16 [n_tok][kv_heads][head_dim_k];
+ * v_src: bf16 [n_tok][kv_heads][head_dim_v] (NULL iff v_from_k); idx_src: bf16
+ * [n_tok][index_dim] (NULL to leave indexer keys untouched).  A token whose request, position
+ * or page entry is out of range is skipped and counted in *bad_dev (device int32, nullable;
+ * not reset by the call).  Does not check refcounts: use tsa_kv_append_check. */
+tsa_status tsa_kv_append(tsa_kv_pool* pool, int32_t layer, int32_t n_tok, const int32_t* req_dev,
+                         const int32_t* pos_dev, const int32_t* page_table_dev, int32_t n_req,
+                         int32_t max_pages, const void* k_src, const void* v_src,
+                         const void* idx_src, int32_t* bad_dev, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * One decode step of one layer: lightning-indexer score for every cached token, top-k
+ * selection, scaled dot-product attention over the selected tokens only.
+ * [GLM5.3 page], opening paragraph: sparse attention attends to the top-k most relevant
+ * tokens, which cuts the bytes SDPA reads, while top-k selection still needs the whole
+ * context in HBM.  Lightning-indexer paragraph:
+ *     score[t] = sum_h w[h] * max(0, qI[h] . kI[t])      (multi-head query, one-head key)
+ * one selection shared by every attention head; a context of at most top_k tokens is kept
+ * whole (dense).  Ties (unspecified on the pages) go to the lower position.
+ * Attention for query head h (KV head g = h / (num_q_heads / num_kv_heads), consecutive
+ * grouping; unspecified on the pages):
+ *     o[h] = softmax_j(sm_scale * q[h] . K[t_j, g]) . V[t_j, g]
+ * ---------------------------------------------------------------------------------- */
+typedef struct tsa_decode_params {
+    int32_t batch;        /* requests B */
+    int32_t num_q_heads;  /* Hq, a multiple of the pool's num_kv_heads */
+    int32_t index_heads;  /* H_I >= 1 (ignored by tsa_sparse_attn_gather) */
+    int32_t top_k;        /* k >= 1 */
+    int32_t max_len;      /* >= every seq_len; sizes the score buffer */
+    float sm_scale;       /* logit scale, e.g. 1/sqrt(head_dim_k) */
+} tsa_decode_params;
+
+/* Workspace bytes the calls below need for these parameters (device memory, caller-owned,
+ * 256-byte aligned, contents need not be initialised). */
+tsa_status tsa_sparse_decode_workspace(const tsa_kv_pool* pool, const tsa_decode_params* p,
+                                       size_t* bytes);
+
+/* Indexer scores only.  qidx_dev: bf16 [B][H_I][index_dim]; widx_dev: fp32 [H_I];
+ * seq_lens_dev: int32 [B]; scores_dev: fp32 [B][ld] with ld >= max_len; entries at
+ * t >= seq_len are left untouched.  Scores are accumulated in fp32 (exact for integer-valued
+ * inputs whose products and sums stay below 2^24). */
+tsa_status tsa_indexer_scores(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                              const void* qidx_dev, const float* widx_dev,
+                              const int32_t* page_table_dev, int32_t max_pages,
+                              const int32_t* seq_lens_dev, float* scores_dev, int32_t ld,
+                              void* stream);
+
+/* Top-k of precomputed scores: fp32 [B][ld]; topk_dev: int32 [B][top_k], ascending
+ * positions, -1 after the min(seq_len, top_k) selected ones.  NaN ranks above +inf. */
+tsa_status tsa_topk(const tsa_decode_params* p, const float* scores_dev, int32_t ld,
+                    const int32_t* seq_lens_dev, int32_t* topk_dev, void* stream);
+
+/* Scores + top-k (the indexer half of the step). */
+tsa_status tsa_indexer_topk(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                            const void* qidx_dev, const float* widx_dev,
+                            const int32_t* page_table_dev, int32_t max_pages,
+                            const int32_t* seq_lens_dev, int32_t* topk_dev, void* workspace,
+                            size_t ws_bytes, void* stream);
+
+/* Attention over given positions (the SDPA half).  q_dev: bf16 [B][Hq][head_dim_k];
+ * topk_dev: int32 [B][top_k] positions (any order; entries < 0 or >= seq_len are ignored);
+ * out_dev: fp32 [B][Hq][head_dim_v].  A request with no valid position gets zeros. */
+tsa_status tsa_sparse_attn_gather(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                                  const void* q_dev, const int32_t* topk_dev,
+                                  const int32_t* page_table_dev, int32_t max_pages,
+                                  const int32_t* seq_lens_dev, float* out_dev, void* workspace,
+                                  size_t ws_bytes, void* stream);
+
+/* The whole step: scores, top-k, attention.  topk_dev (nullable) receives the selection. */
+tsa_status tsa_sparse_decode_attn(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                                  const void* q_dev, const void* qidx_dev, const float* widx_dev,
+                                  const int32_t* page_table_dev, int32_t max_pages,
+                                  const int32_t* seq_lens_dev, float* out_dev, int32_t* topk_dev,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSA_H */

@@ -119,8 +119,12 @@ def _rng(seed: int, w: Workload, stream: int, *more: int) -> np.random.Generator
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 to bf16 (nearest, ties to even); return the uint16 bit patterns."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    r = ((u >> 16) & 1) + np.uint32(0x7FFF)
-    return ((u + r) >> 16).astype(np.uint16)
+    r = np.right_shift(u, np.uint32(16))
+    np.bitwise_and(r, np.uint32(1), out=r)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    return r.astype(np.uint16)
 
 
 def lens(w: Workload, seed: int = 0) -> np.ndarray:

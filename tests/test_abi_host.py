@@ -1,0 +1,199 @@
+"""libtsa host-side tests (no GPU): exported symbols, page tables against the oracle, refcounts,
+error codes.  The pool here is metadata-only (no device memory), so nothing is launched."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import paging
+
+tsa = pytest.importorskip("top_sparse_attention_amd")
+from top_sparse_attention_amd import _lib  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _have_lib():
+    try:
+        _lib.load()
+        return True
+    except ImportError:
+        return False
+
+
+pytestmark = pytest.mark.skipif(not _have_lib(), reason="libtsa.so not built")
+
+
+def _declared():
+    names = set()
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(tsa_\w+)\s*\(", text, re.M))
+    return names
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 18, names
+    lib = C.CDLL(_lib.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing
+    assert set(_lib.SIGNATURES) >= names
+
+
+def test_abi_version():
+    assert tsa.abi_version() == 1
+
+
+def _pool(n, P, **kw):
+    return tsa.KvPool(n, P, kw.pop("kv_heads", 1), kw.pop("dk", 64), kw.pop("dv", 64),
+                      allocate=False, **kw)
+
+
+def test_worked_example_tables_match_oracle():
+    lens = [403, 96, 241, 30, 176]
+    pool = _pool(66, 16)
+    table, num, saved = pool.build_tables(lens, 26)
+    ref = paging.build_page_tables(lens, 16, np.arange(66), max_pages=26)
+    assert np.array_equal(table, ref["table"]) and np.array_equal(num, ref["num_pages"])
+    assert num.sum() == 61 and saved == 0
+    assert pool.usage() == (5, 61)
+
+
+@pytest.mark.parametrize("name", ["tiny_b5", "gqa_b32_8k", "mla_b64_32k", "prefix_b128_16k"])
+def test_workload_tables_match_oracle(name):
+    w = synth.get(name)
+    lens = synth.lens(w, 0)
+    fo = synth.free_order(w, 0)
+    grp, plen = synth.prefix_groups(w)
+    maxp = -(-int(lens.max()) // w.page_size)
+    pool = tsa.KvPool(w.pool_pages, w.page_size, w.num_kv_heads, w.head_dim_k, w.head_dim_v,
+                      v_from_k=w.v_from_k, index_dim=w.index_dim, free_order=fo, allocate=False)
+    table, num, saved = pool.build_tables(lens, maxp, grp, plen)
+    ref = paging.build_page_tables(lens, w.page_size, fo, grp, plen, max_pages=maxp)
+    assert np.array_equal(table, ref["table"])
+    assert np.array_equal(num, ref["num_pages"])
+    assert saved == ref["saved"]
+    if name == "prefix_b128_16k":
+        assert saved == 127 * (16384 // 64) == 32512
+    for p in np.unique(table[table >= 0])[:50]:
+        assert pool.refcount(int(p)) == ref["refcount"][p]
+
+
+def test_sharing_worked_example_and_boundaries():
+    lens = [403, 96, 241, 30, 176]
+    grp = [0, 0, 0, -1, -1]
+    for prefix, used in [(64, 53), (15, 61), (16, 59)]:
+        pool = _pool(70, 16)
+        table, num, saved = pool.build_tables(lens, 26, grp, [prefix])
+        ref = paging.build_page_tables(lens, 16, np.arange(70), grp, [prefix], max_pages=26)
+        assert np.array_equal(table, ref["table"])
+        assert pool.usage()[1] == used == ref["pages_in_use"]
+        assert saved == paging.prefix_pages_saved(3, prefix, 16)
+
+
+def test_out_of_pages_is_all_or_nothing():
+    pool = _pool(60, 16)
+    with pytest.raises(tsa.TsaError) as e:
+        pool.build_tables([403, 96, 241, 30, 176], 26)
+    assert e.value.status == _lib.TSA_ERR_OUT_OF_PAGES
+    assert pool.usage() == (60, 0)
+
+
+def test_grow_and_release_match_oracle():
+    perm = np.random.default_rng(4).permutation(40).astype(np.int32)
+    pool = _pool(40, 16, free_order=perm)
+    lens = [16, 17, 5]
+    table, num, _ = pool.build_tables(lens, 4)
+    ref = paging.build_page_tables(lens, 16, perm, max_pages=4)
+    new = [33, 17, 40]
+    pool.grow_tables(table, num, new)
+    g = paging.grow_page_tables(ref["table"], ref["num_pages"], new, 16, ref["free"])
+    assert np.array_equal(table, g["table"]) and np.array_equal(num, g["num_pages"])
+    with pytest.raises(tsa.TsaError) as e:
+        pool.grow_tables(table, num, [10, 17, 40])          # shrink
+    assert e.value.status == _lib.TSA_ERR_INVALID
+    with pytest.raises(tsa.TsaError) as e:
+        pool.grow_tables(table, num, [65, 65, 65])          # more than max_pages (4 x 16)
+    assert e.value.status == _lib.TSA_ERR_INVALID
+    free0, used0 = pool.usage()
+    pool.release_tables(table, num)
+    assert pool.usage() == (40, 0) and used0 == int(num.sum())
+    with pytest.raises(tsa.TsaError):
+        pool.release_tables(table, num)                     # double release
+
+
+def test_shared_release_keeps_pages_until_last():
+    pool = _pool(20, 16)
+    table, num, _ = pool.build_tables([40, 40], 3, [0, 0], [32])
+    assert pool.refcount(int(table[0, 0])) == 2
+    pool.release_tables(table[:1].copy(), num[:1].copy())
+    assert pool.refcount(int(table[0, 0])) == 1
+    pool.release_tables(table[1:].copy(), num[1:].copy())
+    assert pool.usage() == (20, 0)
+
+
+def test_append_check():
+    pool = _pool(20, 16)
+    table, num, _ = pool.build_tables([40, 40], 3, [0, 0], [32])
+    pool.append_check([0, 1], [39, 32], table, num)         # third page is private
+    with pytest.raises(tsa.TsaError) as e:
+        pool.append_check([1], [31], table, num)            # second page is shared
+    assert e.value.status == _lib.TSA_ERR_SHARED_PAGE_WRITE
+    with pytest.raises(tsa.TsaError) as e:
+        pool.append_check([0], [48], table, num)            # beyond the allocated pages
+    assert e.value.status == _lib.TSA_ERR_INVALID
+    with pytest.raises(tsa.TsaError) as e:
+        pool.append_check([2], [0], table, num)
+    assert e.value.status == _lib.TSA_ERR_INVALID
+
+
+def test_invalid_arguments():
+    with pytest.raises(tsa.TsaError):
+        _pool(0, 16)
+    with pytest.raises(tsa.TsaError):
+        tsa.KvPool(10, 16, 1, 60, 64, allocate=False)        # head dim not a multiple of 8
+    with pytest.raises(tsa.TsaError):
+        tsa.KvPool(10, 16, 1, 64, 128, v_from_k=True, allocate=False)
+    with pytest.raises(ValueError):
+        _pool(10, 16, free_order=np.arange(9))
+    with pytest.raises(tsa.TsaError):
+        _pool(3, 16, free_order=np.array([0, 0, 1]))
+    pool = _pool(10, 16)
+    with pytest.raises(tsa.TsaError):
+        pool.build_tables([10, 20], 2, [0, 0], [16])         # shorter than its prefix
+    with pytest.raises(tsa.TsaError):
+        pool.build_tables([-1], 2)
+
+
+def test_pool_bytes_exact():
+    pool = tsa.KvPool(32832, 64, 1, 576, 512, v_from_k=True, index_dim=128, allocate=False)
+    k, v, i = pool.bytes
+    assert k == 32832 * 64 * 576 * 2 and v == 0 and i == 32832 * 64 * 128 * 2
+
+
+def test_device_calls_refuse_metadata_pool():
+    pool = _pool(10, 16, index_dim=32)
+    p = tsa.decode_params(1, 8, 4, 16, 0.125)
+    n = tsa.workspace_bytes(pool, p)
+    assert n > 0
+    with pytest.raises(tsa.TsaError) as e:
+        tsa.sparse_decode_attn(pool, 0, p, None, None, None, _FakeDev(1), None, None, None,
+                               stream=0)
+    assert e.value.status == _lib.TSA_ERR_INVALID
+
+
+class _FakeDev:
+    """Stands in for a device tensor in argument-validation tests (never dereferenced)."""
+    def __init__(self, max_pages):
+        self.shape = (1, max_pages)
+
+    def is_contiguous(self):
+        return True
+
+    def data_ptr(self):
+        return 0

@@ -1,0 +1,257 @@
+"""GPU parity: every kernel of the decode step against the CPU oracle, through the C ABI.
+
+Bar: page tables, pool placement, indexer scores and top-k index sets bit-exact; attention
+output within 2e-3 normwise relative error per (request, head) row (max_{row} ||o - ref||_inf /
+||ref||_inf), the bound stated for this path.  Inputs are the seeded synthetic workloads; the
+oracle recomputes each checked request from the same draws.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import decode, indexer, paging, sdpa, topk as otopk
+from oracle.bf16 import to_f64
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+ATOL_REL = 2e-3
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def tsa():
+    _need_gpu()
+    import top_sparse_attention_amd as m
+    m.load()
+    return m
+
+
+_STAGED = {}
+
+
+def staged(name, **kw):
+    from top_sparse_attention_amd import workload
+    key = (name, tuple((k, v.tobytes() if isinstance(v, np.ndarray) else v) for k, v in sorted(kw.items())))
+    if key not in _STAGED:
+        print(f"[stage] {name} {kw}", flush=True)
+        _STAGED[key] = workload.stage(synth.get(name), **kw)
+    return _STAGED[key]
+
+
+def _oracle_request(st, b):
+    w = st.w
+    L = int(st.lens[b])
+    kidx, kk, vv = synth.request_tokens(w, st.seed, b, L)
+    s, sel, o = decode.request_step(st.q_np[b], st.qidx_np[b], st.widx_np, kidx, kk, vv, w.top_k,
+                                    w.sm_scale, v_from_k_dims=w.head_dim_v if w.v_from_k else 0)
+    return s, sel, o
+
+
+def _scores_gpu(tsa, st):
+    ld = max(64, -(-st.params.max_len // 64) * 64)
+    sc = torch.full((len(st.lens), ld), float("nan"), dtype=torch.float32, device="cuda")
+    tsa.indexer_scores(st.pool, 0, st.params, st.qidx, st.widx, st.table_dev, st.lens_dev, sc)
+    torch.cuda.synchronize()
+    return sc
+
+
+def _check_request(st, b, scores_gpu=None):
+    s_ref, sel_ref, o_ref = _oracle_request(st, b)
+    L = int(st.lens[b])
+    if scores_gpu is not None:
+        got = scores_gpu[b, :L].cpu().numpy()
+        assert np.array_equal(got.astype(np.float64), s_ref.astype(np.float64)), f"scores differ, request {b}"
+    tk = st.topk[b].cpu().numpy()
+    exp = np.full(st.w.top_k, -1, dtype=np.int32)
+    exp[:len(sel_ref)] = sel_ref
+    assert np.array_equal(tk, exp), f"top-k differs, request {b}"
+    o = st.out[b].double().cpu().numpy()
+    err = sdpa.normwise_rel_err(o, o_ref)
+    assert err < ATOL_REL, f"attention error {err} on request {b}"
+    return err
+
+
+@pytest.mark.parametrize("name", ["tiny_b5", "gqa_b32_8k", "prefix_b128_16k"])
+def test_step_matches_oracle(tsa, name):
+    st = staged(name)
+    sc = _scores_gpu(tsa, st)
+    st.step()
+    torch.cuda.synchronize()
+    reqs = range(len(st.lens)) if len(st.lens) <= 32 else range(0, len(st.lens), 9)
+    errs = [_check_request(st, b, sc) for b in reqs]
+    print(f"{name}: max normwise attention error {max(errs):.3e}")
+
+
+def test_tables_match_oracle(tsa):
+    for name in ["tiny_b5", "gqa_b32_8k", "prefix_b128_16k"]:
+        st = staged(name)
+        w = st.w
+        grp, plen = synth.prefix_groups(w)
+        ref = paging.build_page_tables(st.lens, w.page_size, synth.free_order(w, 0), grp, plen,
+                                       max_pages=st.max_pages)
+        assert np.array_equal(st.table, ref["table"]) and st.saved == ref["saved"]
+
+
+@pytest.mark.parametrize("name", ["tiny_b5", "gqa_b32_8k"])
+def test_pool_placement(tsa, name):
+    """Each logical token sits in the physical slot the oracle's table assigns."""
+    st = staged(name)
+    w = st.w
+    ref = paging.build_page_tables(st.lens, w.page_size, synth.free_order(w, 0), max_pages=st.max_pages)
+    kpool = st.pool.k.view(torch.int16).view(-1, w.num_kv_heads, w.head_dim_k)
+    ipool = st.pool.idx.view(torch.int16).view(-1, w.index_dim)
+    for b in [0, len(st.lens) - 1]:
+        L = int(st.lens[b])
+        kidx, kk, _ = synth.request_tokens(w, 0, b, L)
+        t = np.unique(np.linspace(0, L - 1, 50).astype(int))
+        slots = torch.tensor([paging.physical_slot(ref["table"], b, int(x), w.page_size) for x in t],
+                             device="cuda")
+        assert np.array_equal(kpool[slots].cpu().numpy().view(np.uint16), kk[t])
+        assert np.array_equal(ipool[slots].cpu().numpy().view(np.uint16), kidx[t])
+
+
+def test_free_order_invariance(tsa):
+    """Physical placement must not change any result (the slot translation is the library's)."""
+    w = synth.get("gqa_b32_8k")
+    a = staged("gqa_b32_8k")
+    b = staged("gqa_b32_8k", free_order=np.arange(w.pool_pages, dtype=np.int32)[::-1].copy())
+    for st in (a, b):
+        st.step(append=False)
+    torch.cuda.synchronize()
+    assert not np.array_equal(a.table, b.table)
+    assert torch.equal(a.topk, b.topk)
+    assert torch.equal(a.out, b.out)
+
+
+def test_prefix_alias_vs_copy(tsa):
+    """Aliased prefix pages and private copies of the same prefix give identical results."""
+    a = staged("prefix_b128_16k", batch=6)
+    b = staged("prefix_b128_16k", batch=6, share_prefix=False)
+    assert a.saved == 5 * 256 and b.saved == 0
+    for st in (a, b):
+        st.step(append=False)
+    torch.cuda.synchronize()
+    assert torch.equal(a.topk, b.topk)
+    assert torch.equal(a.out, b.out)
+
+
+@pytest.mark.parametrize("P", [48, 16])
+def test_edge_lengths_and_page_sizes(tsa, P):
+    lens = np.array([0, 1, 63, 512, 513, 1000, 4099, 77], dtype=np.int32)
+    st = staged("gqa_b32_8k", lens=lens, page_size=P)
+    sc = _scores_gpu(tsa, st)
+    st.step(append=False)
+    torch.cuda.synchronize()
+    for b in range(len(lens)):
+        if lens[b] == 0:
+            assert (st.topk[b] == -1).all() and (st.out[b] == 0).all()
+            continue
+        _check_request(st, b, sc)
+
+
+def test_multihead_indexer(tsa):
+    st = staged("gqa_b32_8k", batch=4, index_heads=4)
+    assert st.params.index_heads == 4
+    sc = _scores_gpu(tsa, st)
+    for b in range(4):
+        L = int(st.lens[b])
+        kidx, _, _ = synth.request_tokens(st.w, 0, b, L)
+        ref = indexer.scores_bf16(st.qidx_np[b], st.widx_np, kidx)
+        assert np.array_equal(sc[b, :L].cpu().numpy().astype(np.float64), ref.astype(np.float64))
+
+
+def test_topk_kernel_ties_and_lengths(tsa):
+    """Top-k on crafted scores: heavy ties, every length class, up to 65536 positions."""
+    rng = np.random.default_rng(11)
+    lens = np.array([0, 5, 64, 65, 1000, 4096, 33000, 65536], dtype=np.int32)
+    k = 64
+    ld = 65536
+    s = np.full((len(lens), ld), np.nan, dtype=np.float32)
+    for i, L in enumerate(lens):
+        s[i, :L] = rng.integers(0, 3 + i, size=L).astype(np.float32)
+    s[6, :33000] = 7.0                                   # all equal: first k positions
+    s[7, :100] = -1.5                                    # negatives and a distinct max
+    s[7, 65535] = 1e30
+    p = tsa.decode_params(len(lens), 8, k, ld, 1.0)
+    out = torch.empty((len(lens), k), dtype=torch.int32, device="cuda")
+    tsa.topk(p, torch.from_numpy(s).cuda(), torch.from_numpy(lens).cuda(), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for i, L in enumerate(lens):
+        assert np.array_equal(got[i], otopk.select_padded(s[i, :L], k)), f"row {i}"
+
+
+def test_topk_random_floats(tsa):
+    rng = np.random.default_rng(12)
+    B, L, k = 16, 20000, 2048
+    s = rng.standard_normal((B, L)).astype(np.float32)
+    s[:, ::7] = np.round(s[:, ::7], 1)                   # some duplicated values
+    lens = rng.integers(1, L + 1, size=B).astype(np.int32)
+    p = tsa.decode_params(B, 8, k, L, 1.0)
+    out = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    tsa.topk(p, torch.from_numpy(s).cuda(), torch.from_numpy(lens).cuda(), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(got[b], otopk.select_padded(s[b, :lens[b]], k)), f"row {b}"
+
+
+def test_gather_given_positions(tsa):
+    """Attention over caller-given positions, with invalid entries to skip."""
+    st = staged("tiny_b5")
+    w = st.w
+    rng = np.random.default_rng(3)
+    idx = np.full((5, w.top_k), -1, dtype=np.int32)
+    for b in range(5):
+        L = int(st.lens[b])
+        n = min(L, 40)
+        idx[b, :n] = rng.choice(L, size=n, replace=False)
+        idx[b, n:n + 3] = [L, L + 100, -7]               # out of range: ignored
+    out = torch.empty_like(st.out)
+    tsa.sparse_attn_gather(st.pool, 0, st.params, st.q, torch.from_numpy(idx).cuda(), st.table_dev,
+                           st.lens_dev, out, st.workspace)
+    torch.cuda.synchronize()
+    for b in range(5):
+        L = int(st.lens[b])
+        _, kk, vv = synth.request_tokens(w, 0, b, L)
+        sel = idx[b][(idx[b] >= 0) & (idx[b] < L)]
+        ref = decode.attend_positions(st.q_np[b], kk, vv, sel, w.sm_scale)
+        assert sdpa.normwise_rel_err(out[b].double().cpu().numpy(), ref) < ATOL_REL
+
+
+def test_append_skips_bad_tokens(tsa):
+    st = staged("tiny_b5")
+    w = st.w
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    before = st.pool.k.clone()
+    req = torch.tensor([7, 0, -1, 1], dtype=torch.int32, device="cuda")
+    pos = torch.tensor([0, 5000, 0, -3], dtype=torch.int32, device="cuda")
+    k = torch.zeros((4, w.num_kv_heads, w.head_dim_k), dtype=torch.int16, device="cuda")
+    v = torch.zeros((4, w.num_kv_heads, w.head_dim_v), dtype=torch.int16, device="cuda")
+    st.pool.append(0, req, pos, st.table_dev, 5, k, v, None, bad_dev=bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 4
+    assert torch.equal(before, st.pool.k)
+
+
+def test_mla_full_size_sampled(tsa):
+    """The benchmark's workload (64 requests x 32768 tokens, top-2048, one 576-dim latent head
+    for 64 query heads) in the benchmark's launch configuration; sampled requests checked
+    whole against the oracle, all requests checked for the dense-selection invariants."""
+    st = staged("mla_b64_32k")
+    sc = _scores_gpu(tsa, st)
+    st.step()
+    torch.cuda.synchronize()
+    errs = [_check_request(st, b, sc) for b in [0, 21, 42, 63]]
+    print(f"mla_b64_32k: max normwise attention error {max(errs):.3e}")
+    tk = st.topk.cpu().numpy()
+    assert (np.diff(tk, axis=1) > 0).all() and tk.min() >= 0 and tk.max() < 32768
+    assert torch.isfinite(st.out).all()

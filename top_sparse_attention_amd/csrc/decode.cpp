@@ -1,0 +1,199 @@
+// Host side of the decode step: argument checks, workspace carve-up, launches on the caller's
+// stream.  The step is the GLM5.3 sparse-attention page's DSA decode: lightning-indexer score
+// of every cached token, top-k selection, attention over the selected tokens only.
+#include <algorithm>
+
+#include "tsa_internal.h"
+
+using tsa::fail;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+int scores_ld(int max_len) { return int(tsa::align_up(size_t(std::max(max_len, 1)), 64)); }
+
+struct WsLayout {
+    size_t scores = 0, topk = 0, partial = 0, total = 0;
+};
+
+WsLayout layout(const tsa_kv_pool& pool, const tsa_decode_params& p, bool with_attn) {
+    WsLayout w;
+    size_t off = 0;
+    w.scores = off;
+    off += tsa::align_up(size_t(p.batch) * scores_ld(p.max_len) * sizeof(float), kAlign);
+    w.topk = off;
+    off += tsa::align_up(size_t(p.batch) * p.top_k * sizeof(int32_t), kAlign);
+    w.partial = off;
+    if (with_attn) off += tsa::align_up(tsa::plan_attention(pool, p).partial_bytes, kAlign);
+    w.total = off;
+    return w;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+tsa_status check_common(const tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                        const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens) {
+    if (!pool) return fail(TSA_ERR_INVALID, "pool is NULL");
+    if (!pool->k) return fail(TSA_ERR_INVALID, "pool has no device memory");
+    if (!p) return fail(TSA_ERR_INVALID, "params is NULL");
+    if (layer < 0 || layer >= pool->d.num_layers) return fail(TSA_ERR_INVALID, "layer out of range");
+    if (p->batch < 0 || p->max_len < 0 || p->top_k < 1 || max_pages < 0)
+        return fail(TSA_ERR_INVALID, "batch, max_len, max_pages must be >= 0 and top_k >= 1");
+    if (p->num_q_heads <= 0 || p->num_q_heads % pool->d.num_kv_heads)
+        return fail(TSA_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
+    if (int64_t(p->max_len) > int64_t(max_pages) * pool->d.page_size)
+        return fail(TSA_ERR_INVALID, "max_len exceeds max_pages * page_size");
+    if (p->batch > 0 && (!page_table || !seq_lens)) return fail(TSA_ERR_INVALID, "NULL page table or lengths");
+    return TSA_OK;
+}
+
+tsa_status check_indexer(const tsa_kv_pool* pool, const tsa_decode_params* p, const void* qidx,
+                         const float* widx) {
+    const int D = pool->d.index_dim;
+    if (!D || !pool->idx) return fail(TSA_ERR_INVALID, "pool has no indexer keys");
+    if (!is_pow2(D / 8) || D / 8 > 64) return fail(TSA_ERR_UNSUPPORTED, "index_dim must be 8 x a power of two, <= 512");
+    if (p->index_heads < 1 || p->index_heads > 8) return fail(TSA_ERR_UNSUPPORTED, "index_heads must be in 1..8");
+    if (p->batch > 0 && (!qidx || !widx)) return fail(TSA_ERR_INVALID, "NULL indexer query or weights");
+    return TSA_OK;
+}
+
+tsa_status check_topk(const tsa_decode_params* p) {
+    if (!tsa::topk_supported(p->max_len)) return fail(TSA_ERR_UNSUPPORTED, "max_len above 65536 tokens");
+    return TSA_OK;
+}
+
+tsa_status check_attn(const tsa_kv_pool* pool, const tsa_decode_params* p, const void* q, float* out) {
+    std::string why;
+    if (!tsa::attention_supported(*pool, *p, &why)) return fail(TSA_ERR_UNSUPPORTED, why);
+    if (p->batch > 0 && (!q || !out)) return fail(TSA_ERR_INVALID, "NULL query or output");
+    return TSA_OK;
+}
+
+tsa_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+    if (ws_bytes < need) return fail(TSA_ERR_CAPACITY, "workspace of " + std::to_string(ws_bytes) +
+                                                           " bytes, need " + std::to_string(need));
+    if (need && !ws) return fail(TSA_ERR_INVALID, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(TSA_ERR_INVALID, "workspace not 256-byte aligned");
+    return TSA_OK;
+}
+
+char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+}  // namespace
+
+extern "C" {
+
+tsa_status tsa_sparse_decode_workspace(const tsa_kv_pool* pool, const tsa_decode_params* p,
+                                       size_t* bytes) {
+    if (!pool || !p || !bytes) return fail(TSA_ERR_INVALID, "NULL argument");
+    if (p->batch < 0 || p->max_len < 0 || p->top_k < 1) return fail(TSA_ERR_INVALID, "bad params");
+    if (p->num_q_heads <= 0 || p->num_q_heads % pool->d.num_kv_heads)
+        return fail(TSA_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
+    std::string why;
+    const bool attn = tsa::attention_supported(*pool, *p, &why);
+    *bytes = layout(*pool, *p, attn).total;
+    return TSA_OK;
+}
+
+tsa_status tsa_indexer_scores(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                              const void* qidx_dev, const float* widx_dev,
+                              const int32_t* page_table_dev, int32_t max_pages,
+                              const int32_t* seq_lens_dev, float* scores_dev, int32_t ld,
+                              void* stream) {
+    tsa_status st = check_common(pool, layer, p, page_table_dev, max_pages, seq_lens_dev);
+    if (st) return st;
+    if ((st = check_indexer(pool, p, qidx_dev, widx_dev))) return st;
+    if (ld < p->max_len) return fail(TSA_ERR_INVALID, "ld < max_len");
+    if (p->batch == 0 || p->max_len == 0) return TSA_OK;
+    if (!scores_dev) return fail(TSA_ERR_INVALID, "scores is NULL");
+    hipError_t e = tsa::launch_indexer_scores(*pool, layer, *p, qidx_dev, widx_dev, page_table_dev,
+                                              max_pages, seq_lens_dev, scores_dev, ld,
+                                              static_cast<hipStream_t>(stream));
+    return tsa::hip_check(e, "indexer_score launch");
+}
+
+tsa_status tsa_topk(const tsa_decode_params* p, const float* scores_dev, int32_t ld,
+                    const int32_t* seq_lens_dev, int32_t* topk_dev, void* stream) {
+    if (!p) return fail(TSA_ERR_INVALID, "params is NULL");
+    if (p->batch < 0 || p->max_len < 0 || p->top_k < 1) return fail(TSA_ERR_INVALID, "bad params");
+    if (ld < p->max_len) return fail(TSA_ERR_INVALID, "ld < max_len");
+    tsa_status st = check_topk(p);
+    if (st) return st;
+    if (p->batch == 0) return TSA_OK;
+    if (!scores_dev || !seq_lens_dev || !topk_dev) return fail(TSA_ERR_INVALID, "NULL array");
+    hipError_t e = tsa::launch_topk(*p, scores_dev, ld, seq_lens_dev, topk_dev, static_cast<hipStream_t>(stream));
+    return tsa::hip_check(e, "topk launch");
+}
+
+tsa_status tsa_indexer_topk(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                            const void* qidx_dev, const float* widx_dev,
+                            const int32_t* page_table_dev, int32_t max_pages,
+                            const int32_t* seq_lens_dev, int32_t* topk_dev, void* workspace,
+                            size_t ws_bytes, void* stream) {
+    tsa_status st = check_common(pool, layer, p, page_table_dev, max_pages, seq_lens_dev);
+    if (st) return st;
+    if ((st = check_indexer(pool, p, qidx_dev, widx_dev))) return st;
+    if ((st = check_topk(p))) return st;
+    WsLayout w = layout(*pool, *p, false);
+    if ((st = check_ws(workspace, ws_bytes, w.total))) return st;
+    if (p->batch == 0) return TSA_OK;
+    if (!topk_dev) return fail(TSA_ERR_INVALID, "topk is NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* scores = reinterpret_cast<float*>(at(workspace, w.scores));
+    const int ld = scores_ld(p->max_len);
+    hipError_t e = tsa::launch_indexer_scores(*pool, layer, *p, qidx_dev, widx_dev, page_table_dev,
+                                              max_pages, seq_lens_dev, scores, ld, s);
+    if (e == hipSuccess) e = tsa::launch_topk(*p, scores, ld, seq_lens_dev, topk_dev, s);
+    return tsa::hip_check(e, "indexer_topk launch");
+}
+
+tsa_status tsa_sparse_attn_gather(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                                  const void* q_dev, const int32_t* topk_dev,
+                                  const int32_t* page_table_dev, int32_t max_pages,
+                                  const int32_t* seq_lens_dev, float* out_dev, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+    tsa_status st = check_common(pool, layer, p, page_table_dev, max_pages, seq_lens_dev);
+    if (st) return st;
+    if ((st = check_attn(pool, p, q_dev, out_dev))) return st;
+    WsLayout w = layout(*pool, *p, true);
+    if ((st = check_ws(workspace, ws_bytes, w.total))) return st;
+    if (p->batch == 0) return TSA_OK;
+    if (!topk_dev) return fail(TSA_ERR_INVALID, "topk is NULL");
+    tsa::AttnPlan plan = tsa::plan_attention(*pool, *p);
+    hipError_t e = tsa::launch_attention(*pool, layer, *p, plan, q_dev, topk_dev, page_table_dev,
+                                         max_pages, seq_lens_dev, out_dev,
+                                         plan.partial_bytes ? at(workspace, w.partial) : nullptr,
+                                         static_cast<hipStream_t>(stream));
+    return tsa::hip_check(e, "attention launch");
+}
+
+tsa_status tsa_sparse_decode_attn(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                                  const void* q_dev, const void* qidx_dev, const float* widx_dev,
+                                  const int32_t* page_table_dev, int32_t max_pages,
+                                  const int32_t* seq_lens_dev, float* out_dev, int32_t* topk_dev,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+    tsa_status st = check_common(pool, layer, p, page_table_dev, max_pages, seq_lens_dev);
+    if (st) return st;
+    if ((st = check_indexer(pool, p, qidx_dev, widx_dev))) return st;
+    if ((st = check_topk(p))) return st;
+    if ((st = check_attn(pool, p, q_dev, out_dev))) return st;
+    WsLayout w = layout(*pool, *p, true);
+    if ((st = check_ws(workspace, ws_bytes, w.total))) return st;
+    if (p->batch == 0) return TSA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* scores = reinterpret_cast<float*>(at(workspace, w.scores));
+    int32_t* topk = topk_dev ? topk_dev : reinterpret_cast<int32_t*>(at(workspace, w.topk));
+    const int ld = scores_ld(p->max_len);
+    tsa::AttnPlan plan = tsa::plan_attention(*pool, *p);
+    hipError_t e = tsa::launch_indexer_scores(*pool, layer, *p, qidx_dev, widx_dev, page_table_dev,
+                                              max_pages, seq_lens_dev, scores, ld, s);
+    if (e == hipSuccess) e = tsa::launch_topk(*p, scores, ld, seq_lens_dev, topk, s);
+    if (e == hipSuccess)
+        e = tsa::launch_attention(*pool, layer, *p, plan, q_dev, topk, page_table_dev, max_pages,
+                                  seq_lens_dev, out_dev,
+                                  plan.partial_bytes ? at(workspace, w.partial) : nullptr, s);
+    return tsa::hip_check(e, "decode launch");
+}
+
+}  // extern "C"

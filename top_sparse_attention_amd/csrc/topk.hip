@@ -1,0 +1,175 @@
+// Top-k selection of indexer scores: one workgroup per request, radix select in LDS.
+//
+// GLM5.3 sparse-attention page, lightning-indexer paragraph: the score selects the top K
+// tokens; a query with fewer than K tokens stays dense.  Equal scores are ordered by position
+// (lowest first), so the selected set is unique; it is written as ascending positions.
+//
+// Method: scores map to order-preserving 32-bit keys.  Four 8-bit radix passes narrow the key
+// of the k-th largest element (a histogram of the candidate digits per pass, kept in LDS as 16
+// interleaved copies so that lanes hitting the same bin spread over distinct addresses).  After
+// the passes, every element whose key exceeds the threshold is kept, and of the elements equal
+// to it the lowest positions fill the rest; a block-wide scan over positions (each thread
+// owns a contiguous run of positions) yields both the tie ranks and the output offsets, so the
+// output comes out ascending with no sort.
+#include "tsa_internal.h"
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kCopies = 16;
+
+__device__ inline uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive scan over the block in thread order; returns this thread's prefix, total in *total.
+__device__ inline int block_exclusive_scan(int v, int* sh_waves, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) sh_waves[wave] = x;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        int w = threadIdx.x < kWaves ? sh_waves[threadIdx.x] : 0;
+        int s = w;
+#pragma unroll
+        for (int o = 1; o < kWaves; o <<= 1) {
+            int y = __shfl_up(s, o);
+            if ((int)threadIdx.x >= o) s += y;
+        }
+        if (threadIdx.x < kWaves) sh_waves[kWaves + threadIdx.x] = s - w;
+        if (threadIdx.x == kWaves - 1) sh_waves[2 * kWaves] = s;
+    }
+    __syncthreads();
+    int r = sh_waves[kWaves + wave] + x - v;
+    *total = sh_waves[2 * kWaves];
+    __syncthreads();
+    return r;
+}
+
+template <int IPT>
+__global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __restrict__ scores,
+                                                              int ld,
+                                                              const int32_t* __restrict__ seq_lens,
+                                                              int max_len, int k,
+                                                              int32_t* __restrict__ out) {
+    __shared__ uint32_t hist[256 * kCopies];
+    __shared__ int sh_scan[2 * kWaves + 1];
+    __shared__ int sh_sel[4];
+
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    int len = seq_lens[b];
+    len = len < 0 ? 0 : (len > max_len ? max_len : len);
+    int32_t* o = out + int64_t(b) * k;
+    if (len <= k) {  // dense: every position, then padding
+        for (int i = tid; i < k; i += kThreads) o[i] = i < len ? i : -1;
+        return;
+    }
+    const float* s = scores + int64_t(b) * ld;
+    const int base = tid * IPT;
+    uint32_t key[IPT];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) key[i] = (base + i < len) ? order_key(s[base + i]) : 0u;
+
+    uint32_t prefix = 0, mask = 0;
+    int remaining = k;  // how many of the elements matching `prefix` under `mask` to keep
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256 * kCopies; i += kThreads) hist[i] = 0;
+        __syncthreads();
+        const int copy = tid & (kCopies - 1);
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) {
+            if (base + i < len && (key[i] & mask) == prefix)
+                atomicAdd(&hist[((key[i] >> shift) & 255u) * kCopies + copy], 1u);
+        }
+        __syncthreads();
+        // bins in descending digit order: thread j < 256 owns digit 255 - j
+        int c = 0;
+        if (tid < 256) {
+            const int dgt = 255 - tid;
+#pragma unroll
+            for (int j = 0; j < kCopies; ++j) c += hist[dgt * kCopies + ((j + tid) & (kCopies - 1))];
+        }
+        int total;
+        const int above = block_exclusive_scan(c, sh_scan, &total);  // count with a larger digit
+        if (tid < 256 && above < remaining && above + c >= remaining) {
+            sh_sel[0] = 255 - tid;
+            sh_sel[1] = remaining - above;
+            sh_sel[2] = c;
+        }
+        __syncthreads();
+        const uint32_t dgt = sh_sel[0];
+        remaining = sh_sel[1];
+        const int in_bin = sh_sel[2];
+        __syncthreads();
+        prefix |= dgt << shift;
+        mask |= 255u << shift;
+        if (in_bin == remaining) break;  // the whole bin is kept: no finer digit matters
+    }
+
+    // final selection: above the threshold, or equal to it and among the first `remaining`
+    int eq = 0;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) eq += (base + i < len && (key[i] & mask) == prefix);
+    int dummy;
+    int eq_before = block_exclusive_scan(eq, sh_scan, &dummy);
+    int nsel = 0;
+    uint64_t selbits = 0;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        bool v = base + i < len;
+        uint32_t m = key[i] & mask;
+        bool take = false;
+        if (v && m > prefix) take = true;
+        if (v && m == prefix) {
+            take = eq_before < remaining;
+            ++eq_before;
+        }
+        if (take) {
+            selbits |= uint64_t(1) << i;
+            ++nsel;
+        }
+    }
+    int total;
+    int off = block_exclusive_scan(nsel, sh_scan, &total);
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        if (((selbits >> i) & 1) && off < k) o[off++] = base + i;
+    }
+}
+
+template <int IPT>
+void launch_ipt(const tsa_decode_params& p, const float* scores, int ld, const int32_t* seq_lens,
+                int32_t* topk, hipStream_t s) {
+    hipLaunchKernelGGL((topk_radix_kernel<IPT>), dim3(p.batch), dim3(kThreads), 0, s, scores, ld,
+                       seq_lens, p.max_len, p.top_k, topk);
+}
+
+}  // namespace
+
+namespace tsa {
+
+bool topk_supported(int max_len) { return max_len <= 64 * kThreads; }
+
+hipError_t launch_topk(const tsa_decode_params& p, const float* scores, int ld,
+                       const int32_t* seq_lens, int32_t* topk, hipStream_t s) {
+    const int ipt = (p.max_len + kThreads - 1) / kThreads;
+    if (ipt <= 1) launch_ipt<1>(p, scores, ld, seq_lens, topk, s);
+    else if (ipt <= 2) launch_ipt<2>(p, scores, ld, seq_lens, topk, s);
+    else if (ipt <= 4) launch_ipt<4>(p, scores, ld, seq_lens, topk, s);
+    else if (ipt <= 8) launch_ipt<8>(p, scores, ld, seq_lens, topk, s);
+    else if (ipt <= 16) launch_ipt<16>(p, scores, ld, seq_lens, topk, s);
+    else if (ipt <= 32) launch_ipt<32>(p, scores, ld, seq_lens, topk, s);
+    else if (ipt <= 64) launch_ipt<64>(p, scores, ld, seq_lens, topk, s);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace tsa

@@ -1,0 +1,71 @@
+// Internal declarations shared by the host sources and the kernel launchers of libtsa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "tsa.h"
+
+struct tsa_kv_pool {
+    tsa_pool_desc d;
+    void* k = nullptr;
+    void* v = nullptr;
+    void* idx = nullptr;
+    std::vector<int32_t> free_list;  // pages handed out from the front
+    size_t free_head = 0;            // free_list[free_head..] are free
+    std::vector<int32_t> refcount;   // per physical page
+
+    int64_t slots() const { return int64_t(d.num_pages) * d.page_size; }
+    int32_t free_count() const { return int32_t(free_list.size() - free_head); }
+    int32_t pop() { return free_list[free_head++]; }
+    void push(int32_t p) { free_list.push_back(p); }
+    void compact_free();
+};
+
+namespace tsa {
+
+// Sets the thread's last-error message and returns `st`.
+tsa_status fail(tsa_status st, const std::string& msg);
+tsa_status ok();
+tsa_status hip_check(hipError_t e, const char* what);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- kernel launchers (defined in the .hip sources) ----
+
+// One wave per token: copy rows into the pool slot given by the page table.
+hipError_t launch_kv_append(const tsa_kv_pool& pool, int layer, int n_tok, const int32_t* req,
+                            const int32_t* pos, const int32_t* page_table, int n_req,
+                            int max_pages, const void* k_src, const void* v_src,
+                            const void* idx_src, int32_t* bad, hipStream_t s);
+
+// Indexer score of every cached token (fp32 [B][ld]).
+hipError_t launch_indexer_scores(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
+                                 const void* qidx, const float* widx, const int32_t* page_table,
+                                 int max_pages, const int32_t* seq_lens, float* scores, int ld,
+                                 hipStream_t s);
+
+// Whether the top-k kernel handles this maximum length.
+bool topk_supported(int max_len);
+hipError_t launch_topk(const tsa_decode_params& p, const float* scores, int ld,
+                       const int32_t* seq_lens, int32_t* topk, hipStream_t s);
+
+// Attention planning: how the selected tokens are split across workgroups.
+struct AttnPlan {
+    int kind = 0;         // 0 = VALU grouped-query kernel, 1 = MFMA latent kernel
+    int splits = 1;       // workgroups per (request, KV head) along the selected tokens
+    int chunk = 0;        // selected tokens per split
+    size_t partial_bytes = 0;
+};
+AttnPlan plan_attention(const tsa_kv_pool& pool, const tsa_decode_params& p);
+bool attention_supported(const tsa_kv_pool& pool, const tsa_decode_params& p, std::string* why);
+hipError_t launch_attention(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
+                            const AttnPlan& plan, const void* q, const int32_t* topk,
+                            const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                            float* out, void* partial, hipStream_t s);
+
+}  // namespace tsa

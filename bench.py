@@ -192,7 +192,7 @@ def main():
         "kernels_ms": {"kv_append": round(t_append, 5), "indexer_score": round(t_index, 5),
                        "topk": round(t_topk, 5), "attention": round(t_attn, 5)},
         "roofline": roof(idx_bytes, t_index, "indexer_score.hip", f"indexer_score/{w.name}"),
-        "roofline_attention": dict(roof(attn_bytes, t_attn, "attn_valu.hip", f"attention/{w.name}"),
+        "roofline_attention": dict(roof(attn_bytes, t_attn, ("attn_mfma.hip" if w.v_from_k else "attn_valu.hip"), f"attention/{w.name}"),
                                    flops=attn_flops,
                                    tflops=round(attn_flops / (t_attn * 1e-3) / 1e12, 2)),
         "cpu_baseline": None,

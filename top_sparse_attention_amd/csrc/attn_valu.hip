@@ -311,6 +311,14 @@ bool attention_supported(const tsa_kv_pool& pool, const tsa_decode_params& p, st
 AttnPlan plan_attention(const tsa_kv_pool& pool, const tsa_decode_params& p) {
     AttnPlan plan;
     const tsa_pool_desc& d = pool.d;
+    if (mfma_latent_applicable(pool, p)) {
+        plan.kind = 1;
+        plan.chunk = mfma_latent_chunk(p, &plan.splits);
+        plan.partial_bytes = plan.splits > 1 ? size_t(p.batch) * p.num_q_heads * plan.splits *
+                                                   (size_t(d.head_dim_v) + 2) * sizeof(float)
+                                             : 0;
+        return plan;
+    }
     const int G = p.num_q_heads / d.num_kv_heads;
     const int T = pick_tile(G, d.head_dim_k, d.head_dim_v, d.v_from_k);
     const int units = p.batch * d.num_kv_heads;
@@ -325,6 +333,9 @@ AttnPlan plan_attention(const tsa_kv_pool& pool, const tsa_decode_params& p) {
                                          : 0;
     return plan;
 }
+
+hipError_t launch_valu(const AttnArgs& a, const tsa_kv_pool& pool, const tsa_decode_params& p,
+                       const AttnPlan& plan, hipStream_t s);
 
 hipError_t launch_attention(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                             const AttnPlan& plan, const void* q, const int32_t* topk,
@@ -362,6 +373,22 @@ hipError_t launch_attention(const tsa_kv_pool& pool, int layer, const tsa_decode
     a.part_ml = static_cast<float*>(partial);
     a.part_acc = a.part_ml ? a.part_ml + n_part * 2 : nullptr;
 
+    hipError_t e;
+    if (plan.kind == 1) {
+        e = launch_attention_mfma(pool, layer, p, plan, q, topk, page_table, max_pages, seq_lens,
+                                  out, a.part_ml, a.part_acc, s);
+    } else {
+        e = launch_valu(a, pool, p, plan, s);
+    }
+    if (e != hipSuccess || plan.splits == 1) return e;
+    hipLaunchKernelGGL(combine_kernel, dim3(p.batch * p.num_q_heads), dim3(kThreads), 0, s,
+                       a.part_ml, a.part_acc, plan.splits, d.head_dim_v, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_valu(const AttnArgs& a, const tsa_kv_pool& pool, const tsa_decode_params& p,
+                       const AttnPlan& plan, hipStream_t s) {
+    const tsa_pool_desc& d = pool.d;
     const int G = p.num_q_heads / d.num_kv_heads;
     const int T = pick_tile(G, d.head_dim_k, d.head_dim_v, d.v_from_k);
     const size_t smem = valu_smem_bytes(T, G, d.head_dim_k, d.head_dim_v, d.v_from_k);
@@ -373,10 +400,7 @@ hipError_t launch_attention(const tsa_kv_pool& pool, int layer, const tsa_decode
         case 32: e = launch_t<32>(a, nacc, grid, smem, s); break;
         default: e = launch_t<16>(a, nacc, grid, smem, s); break;
     }
-    if (e != hipSuccess || plan.splits == 1) return e;
-    hipLaunchKernelGGL(combine_kernel, dim3(p.batch * p.num_q_heads), dim3(kThreads), 0, s,
-                       a.part_ml, a.part_acc, plan.splits, d.head_dim_v, out);
-    return hipGetLastError();
+    return e;
 }
 
 }  // namespace tsa

@@ -63,6 +63,13 @@ struct AttnPlan {
 };
 AttnPlan plan_attention(const tsa_kv_pool& pool, const tsa_decode_params& p);
 bool attention_supported(const tsa_kv_pool& pool, const tsa_decode_params& p, std::string* why);
+// Matrix-core kernel for the latent (MQA-mode MLA) shape.
+bool mfma_latent_applicable(const tsa_kv_pool& pool, const tsa_decode_params& p);
+int mfma_latent_chunk(const tsa_decode_params& p, int* splits);
+hipError_t launch_attention_mfma(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
+                                 const AttnPlan& plan, const void* q, const int32_t* topk,
+                                 const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                                 float* out, float* part_ml, float* part_acc, hipStream_t s);
 hipError_t launch_attention(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                             const AttnPlan& plan, const void* q, const int32_t* topk,
                             const int32_t* page_table, int max_pages, const int32_t* seq_lens,

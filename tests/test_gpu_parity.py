@@ -255,3 +255,24 @@ def test_mla_full_size_sampled(tsa):
     tk = st.topk.cpu().numpy()
     assert (np.diff(tk, axis=1) > 0).all() and tk.min() >= 0 and tk.max() < 32768
     assert torch.isfinite(st.out).all()
+
+
+def test_mla_large_logits_take_the_rescan_path(tsa):
+    """Queries scaled so that logits span far more than 2^32 between the first tile of a split
+    and later tiles: the latent kernel must detect it, rescan for the true max and still match
+    the oracle (softmax over float64 logits)."""
+    st = staged("mla_b64_32k", batch=2)
+    w = st.w
+    rng = np.random.default_rng(21)
+    q = synth.f32_to_bf16_bits((rng.standard_normal((2, 64, 576)) * 60).astype(np.float32))
+    idx = np.stack([np.sort(rng.choice(int(st.lens[b]), size=w.top_k, replace=False)) for b in range(2)])
+    idx = idx.astype(np.int32)
+    out = torch.empty((2, 64, 512), dtype=torch.float32, device="cuda")
+    tsa.sparse_attn_gather(st.pool, 0, st.params, torch.from_numpy(q.view(np.int16)).cuda(),
+                           torch.from_numpy(idx).cuda(), st.table_dev, st.lens_dev, out, st.workspace)
+    torch.cuda.synchronize()
+    for b in range(2):
+        _, kk, _ = synth.request_tokens(w, 0, b, int(st.lens[b]))
+        ref = decode.attend_positions(q[b], kk, None, idx[b], w.sm_scale, v_from_k_dims=512)
+        err = sdpa.normwise_rel_err(out[b].double().cpu().numpy(), ref)
+        assert err < ATOL_REL, f"request {b}: {err}"

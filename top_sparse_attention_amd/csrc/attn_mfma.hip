@@ -18,9 +18,16 @@
 //       B operand: P taken straight from the S^T accumulators (the contraction runs over the
 //                  tokens in a permuted order; A and B use the same permutation)
 // P is split into bf16 hi + lo parts (two PV MFMAs) so the probabilities keep ~16 bits.
-// Tiles of 64 selected rows are gathered from the page table straight into LDS (global-to-LDS
-// loads, no staging registers), double-buffered: the next tile streams in while the current one
-// is computed.
+//
+// Data movement: tiles of 32 selected rows are gathered from the page table straight into LDS
+// with global-to-LDS loads (no staging registers), into a ring of 4 buffers so that 3 tiles
+// stream in while one is computed.  The loads are issued from inline assembly and waited for
+// with explicit vector-memory counts: the compiler would otherwise wait for every outstanding
+// LDS-bound load before the first LDS read, which serialises the ring.  A tile is stored as two
+// regions: the first DV dims of each row (value dims, DV/8 16-byte chunks, one wave-wide load
+// per row) and the remaining DK-DV dims (8 chunks per row, one load per 8 rows).  Within each
+// region the chunk index is XOR-swizzled with the row so that row-parallel operand reads spread
+// over the LDS banks.
 #include "tsa_internal.h"
 
 namespace {
@@ -29,35 +36,63 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 64;                 // selected rows per tile
+constexpr int kTile = 32;                 // selected rows per tile
+constexpr int kRing = 4;                  // tile buffers in LDS
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kQkAhead = 4;               // QK k-steps whose LDS operands are read ahead
+constexpr float kHeadroom = 32.f;         // log2 headroom of the fixed softmax reference
 
-template <int DK>
+template <int DK, int DV>
 struct Geo {
-    static constexpr int kChunks = DK / 8;                // 16-byte chunks of a row
-    static constexpr int kRowChunks = kChunks + 1;        // +1 padding chunk staggers LDS banks
-    static constexpr int kRowBytes = kRowChunks * 16;
-    static constexpr int kTileBytes = kTile * kRowBytes;
-    // one wave-wide direct load fills 64 consecutive 16-byte LDS chunks; a tile of 64 padded
-    // rows is therefore exactly kRowChunks such loads
-    static constexpr int kLoads = kRowChunks;
+    static constexpr int kChunksA = DV / 8;                 // value-dim chunks of a row
+    static constexpr int kChunksB = (DK - DV) / 8;          // remaining chunks of a row
+    static constexpr int kRowBytesA = DV * 2;
+    static constexpr int kRowBytesB = (DK - DV) * 2;
+    static constexpr int kBytesA = kTile * kRowBytesA;
+    static constexpr int kTileBytes = kTile * (kRowBytesA + kRowBytesB);
+    static constexpr int kRowsPerWaveA = kTile / kWaves;    // one load per row of region A
+    static_assert(kChunksA == 64, "region A rows are one wave-wide load each");
+    static_assert(kChunksB == 8, "region B holds 8 chunks of 8 rows per load");
+    static_assert(kTile / 8 == kWaves, "one region-B load per wave");
 };
+constexpr int kLoadsPerWave = kTile / kWaves + 1;
 
-__device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+// stored chunk position of logical chunk c of tile row r, region A (groups of 16 chunks) and
+// region B (8 chunks per row); both are involutions on c
+__device__ __forceinline__ int swz_a(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int swz_b(int r, int c) { return c ^ (((r >> 1) ^ (r << 2)) & 7); }
 
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Wave-wide global-to-LDS load: lane i's 16 bytes land at lds + 16 * i.
-__device__ inline void load_lds16(const void* gsrc, unsigned char* lds) {
-    __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)((lds_u8*)(lds)),
-                                     16, 0, 0);
+__device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)(p)));
 }
 
-// LDS transpose load of 4 x 16-bit (see the formulation above for the lane mapping).
-__device__ inline uint2 lds_read_tr16(const unsigned char* p) {
+// Wave-wide global-to-LDS load: lane i's 16 bytes land at (uniform) lds + 16 * i.
+__device__ __forceinline__ void load_lds16(const void* gsrc, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gsrc), "s"(lds)
+                 : "memory", "m0");
+}
+
+// Wait until at most N vector-memory instructions of this wave are outstanding.  Emitted as a
+// real s_waitcnt (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their
+// maxima) so that the compiler's own wait tracking sees it too.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS transpose load of 4 x 16-bit.  In each 16-lane group, lane i supplies the address of 4
+// consecutive elements; lane j receives element j%4 of the data addressed by lanes
+// j/4, 4 + j/4, 8 + j/4, 12 + j/4.
+__device__ __forceinline__ uint2 lds_read_tr16(const unsigned char* p) {
     lds_i16x4* lp = (lds_i16x4*)((lds_u8*)(p));
     return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
 }
@@ -77,12 +112,14 @@ struct MfmaArgs {
 
 template <int DK, int DV>
 __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
-    using G = Geo<DK>;
-    constexpr int KS = DK / 32;   // QK k-steps
+    using G = Geo<DK, DV>;
+    constexpr int KS = DK / 32;   // QK k-steps (the first KSA read region A, the rest region B)
+    constexpr int KSA = DV / 32;
     constexpr int DB = DV / 16;   // output dim blocks per wave
     extern __shared__ __align__(16) unsigned char smem[];
-    unsigned char* tiles = smem;                                              // 2 x [kTile][kRowBytes]
-    int32_t* rows = reinterpret_cast<int32_t*>(smem + 2 * G::kTileBytes);   // [chunk] slot or -1
+    unsigned char* ring = smem;                                                // kRing tiles
+    int32_t* flag = reinterpret_cast<int32_t*>(smem + kRing * G::kTileBytes);  // rescan request
+    int32_t* rows = flag + 4;                                                   // [chunk]
 
     const int s_idx = blockIdx.x, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -95,13 +132,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
     const int j0 = s_idx * a.chunk;
     const int j1 = min(j0 + a.chunk, n_sel);
     const int n = max(j1 - j0, 0);
+    const int n_tiles = (n + kTile - 1) / kTile;
 
-    // resolve this split's selected positions to physical rows; zero both tile buffers so rows
-    // that are never loaded (past the selection) hold finite values
+    // resolve this split's selected positions to physical rows (-1 = absent: such rows are
+    // fetched from slot 0 like any other row and masked out of the softmax)
     {
         const int32_t* sel = a.topk + int64_t(b) * a.k;
         const int32_t* pt = a.page_table + int64_t(b) * a.max_pages;
-        for (int j = tid; j < a.chunk; j += kThreads) {
+        for (int j = tid; j < n_tiles * kTile; j += kThreads) {
             int32_t row = -1;
             if (j < n) {
                 const int t = sel[j0 + j];
@@ -112,8 +150,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
             }
             rows[j] = row;
         }
-        for (int i = tid; i < 2 * G::kTileBytes / 16; i += kThreads)
-            reinterpret_cast<uint4*>(tiles)[i] = make_uint4(0, 0, 0, 0);
     }
 
     // queries of this wave's 16 heads, as the B operand of S^T = K Q^T
@@ -127,92 +163,148 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
     f32x4 acc[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;   // running max (log2 units) of head h0 + j16
+    float m_ref = -INFINITY;   // reference max (log2 units) of head h0 + j16
     float l_run = 0.f;         // this lane's share of the running sum
 
-    __syncthreads();
-    const int n_tiles = (n + kTile - 1) / kTile;
+    // lane-constant byte offsets inside a tile:
+    //  QK, region A: row j16 (+16 for the second block), chunk ks*4 + g16 = 16*(ks/4) +
+    //      (4*(ks%4) + g16); the swizzle XORs the low 4 bits with the row's low 4 bits (j16)
+    //  QK, region B: chunk 4*(ks-KSA) + g16 of row j16 (+16), swizzled within the row's 8
+    //  PV: rows r0 = 4*g16 + j16/4 and r0 + 16, dims db*16 + 4*(j16%4): chunk 2*db + b0 =
+    //      16*(db/8) + (2*(db%8) + b0), byte (e0 % 8) * 2 inside it
+    int qk_off[4], qkb_off[KS - KSA], pv_off[8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qk_off[u] = j16 * G::kRowBytesA + swz_a(j16, 4 * u + g16) * 16;
+#pragma unroll
+    for (int u = 0; u < KS - KSA; ++u)
+        qkb_off[u] = G::kBytesA + j16 * G::kRowBytesB + swz_b(j16, 4 * u + g16) * 16;
+    {
+        const int r0 = 4 * g16 + (j16 >> 2);
+        const int e0 = 4 * (j16 & 3);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            pv_off[u] = r0 * G::kRowBytesA + swz_a(r0, 2 * u + (e0 >> 3)) * 16 + (e0 & 7) * 2;
+    }
+    // loads: region A row r = wave*8 + m is one wave-wide load (lane = stored chunk position);
+    // region B rows wave*8 .. wave*8+7 are one load (lane = 8 * row-in-group + stored chunk)
+    const int a_src_chunk = lane;                      // XORed with the row's swizzle per load
+    const int b_row = wave * 8 + (lane >> 3);
+    const int b_src_el = DV + swz_b(b_row, lane & 7) * 8;
 
-    // issue the direct loads of tile t into buffer t & 1: load i of the tile covers padded
-    // chunks 64 i .. 64 i + 63; waves take loads round-robin; padding and absent rows are skipped
+    wait_vm<0>();              // query registers loaded
+    if (tid == 0) *flag = 0;
+    __syncthreads();           // rows[] and the flag visible
+
+    const uint32_t ring_base = lds_addr(ring);
     auto issue_tile = [&](int t) {
-        unsigned char* buf = tiles + (t & 1) * G::kTileBytes;
-        for (int i = wave; i < G::kLoads; i += kWaves) {
-            const int c = i * 64 + lane;
-            const int r = c / G::kRowChunks, col = c - r * G::kRowChunks;
-            const int j = t * kTile + r;
-            const int32_t row = (col < G::kChunks && j < n) ? rows[j] : -1;
-            if (row >= 0) load_lds16(a.kpool + int64_t(row) * DK + col * 8, buf + i * 1024);
+        const uint32_t buf = ring_base + uint32_t((t % kRing) * G::kTileBytes);
+        const int32_t* trow = rows + t * kTile;
+        const int32_t my8 = trow[wave * 8 + (lane & 7)];      // rows wave*8 .. +7, lanes 0..7
+#pragma unroll
+        for (int m = 0; m < G::kRowsPerWaveA; ++m) {
+            const int r = wave * 8 + m;
+            const int32_t row = __builtin_amdgcn_readlane(my8, m);
+            const uint16_t* src = a.kpool + int64_t(row < 0 ? 0 : row) * DK + swz_a(r, a_src_chunk) * 8;
+            load_lds16(src, __builtin_amdgcn_readfirstlane(buf + uint32_t(r * G::kRowBytesA)));
         }
+        const int32_t rowb = trow[b_row];
+        const uint16_t* srcb = a.kpool + int64_t(rowb < 0 ? 0 : rowb) * DK + b_src_el;
+        load_lds16(srcb, __builtin_amdgcn_readfirstlane(buf + uint32_t(G::kBytesA + wave * 1024)));
     };
-    if (n_tiles > 0) issue_tile(0);
 
-    for (int t = 0; t < n_tiles; ++t) {
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile t have landed
-        __syncthreads();                 // everyone's have, and tile t-1 is no longer read
-        if (t + 1 < n_tiles) issue_tile(t + 1);
-        const unsigned char* tile = tiles + (t & 1) * G::kTileBytes;
+    // Softmax reference: the probabilities are exp2(logit - m_ref) with m_ref fixed at the first
+    // tile where the head has a valid token, never rescaled.  Any reference gives the same
+    // softmax as long as exp2 cannot overflow, so a tile whose max exceeds m_ref by more than
+    // kHeadroom (2^32) switches the whole workgroup to a scan that only tracks the true max;
+    // the split is then computed again with m_ref = that max.  Inputs whose logits stay within
+    // 2^32 of the first tile's max take one pass.
+    float m_seen = -INFINITY;  // max logit (log2 units) over the tiles scanned so far
+    for (int pass = 0; pass < 2; ++pass) {
+        bool scan = false;
+        if (n_tiles > 0) issue_tile(0);
+        if (n_tiles > 1) issue_tile(1);
+        if (n_tiles > 2) issue_tile(2);
+        for (int t = 0; t < n_tiles; ++t) {
+            // tile t has landed once at most the loads of tiles t+1, t+2 are still outstanding
+            if (t + 2 < n_tiles) wait_vm<2 * kLoadsPerWave>();
+            else if (t + 1 < n_tiles) wait_vm<kLoadsPerWave>();
+            else wait_vm<0>();
+            __syncthreads();   // every wave's part landed; tile t-1's buffer is free again
+            scan = *flag != 0;
+            if (t + 3 < n_tiles) issue_tile(t + 3);
+            const unsigned char* tile = ring + (t % kRing) * G::kTileBytes;
 
-        // ---- S^T = K Q^T : four 16-token blocks x 16 heads
-        f32x4 s[4];
+            // ---- S^T = K Q^T : two 16-token blocks x 16 heads
+            f32x4 s[2];
+            s[0] = s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            {
+                // operand reads run kQkAhead k-steps ahead of the MFMAs (a register ring); the
+                // scheduling fences keep the compiler from sinking the reads next to their use
+                uint4 kv[kQkAhead][2];
+                auto qk_read = [&](int ks, uint4 (&dst)[2]) {
+                    const unsigned char* base = ks < KSA ? tile + qk_off[ks & 3] + (ks >> 2) * 256
+                                                         : tile + qkb_off[ks - KSA];
+                    const int second = ks < KSA ? 16 * G::kRowBytesA : 16 * G::kRowBytesB;
+                    dst[0] = *reinterpret_cast<const uint4*>(base);
+                    dst[1] = *reinterpret_cast<const uint4*>(base + second);
+                };
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) s[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks < kQkAhead; ++ks) qk_read(ks, kv[ks]);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 qb = as_bf16x8(qreg[ks]);
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-                const uint4 kv = *reinterpret_cast<const uint4*>(
-                    tile + (tb * 16 + j16) * G::kRowBytes + (ks * 32 + g16 * 8) * 2);
-                s[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv), qb, s[tb], 0, 0, 0);
+                for (int ks = 0; ks < KS; ++ks) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    const bf16x8 qb = as_bf16x8(qreg[ks]);
+                    s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks % kQkAhead][0]), qb, s[0], 0, 0, 0);
+                    s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks % kQkAhead][1]), qb, s[1], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (ks + kQkAhead < KS) qk_read(ks + kQkAhead, kv[ks % kQkAhead]);
+                }
             }
-        }
-        // lane holds S^T[token tb*16 + 4*g16 + r][head h0 + j16]
-        const int valid = min(kTile, n - t * kTile);
-        float tmax = -INFINITY;
+            // lane holds S^T[token tb*16 + 4*g16 + r][head h0 + j16]; bit j of `live` = token j
+            // of the tile is a selected, resolvable row
+            const uint64_t live = __ballot(lane < kTile && t * kTile + lane < n &&
+                                           rows[t * kTile + (lane & (kTile - 1))] >= 0);
+            float tmax = -INFINITY;
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+            for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = tb * 16 + g16 * 4 + r;
-                float x = s[tb][r] * a.scale_log2;
-                x = tok < valid ? x : -INFINITY;
-                s[tb][r] = x;
-                tmax = fmaxf(tmax, x);
-            }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = (m_run == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-        float psum = 0.f;
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float p = (s[tb][r] == -INFINITY) ? 0.f : exp2f(s[tb][r] - m_new);
-                s[tb][r] = p;
-                psum += p;
-            }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) acc[i] *= alpha;
+                for (int r = 0; r < 4; ++r) {
+                    const int tok = tb * 16 + g16 * 4 + r;
+                    const float x = ((live >> tok) & 1) ? s[tb][r] * a.scale_log2 : -INFINITY;
+                    s[tb][r] = x;
+                    tmax = fmaxf(tmax, x);
+                }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            m_seen = fmaxf(m_seen, tmax);
+            if (scan) continue;                      // uniform: the flag was read after a barrier
+            if (m_ref == -INFINITY) m_ref = tmax;    // first tile with a valid token for the head
+            if (__ballot(tmax > m_ref + kHeadroom)) *flag = 1;
 
-        // ---- O^T += V^T P^T over two 32-token k-steps
+            float psum = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            // B operand: P^T[kappa][head], kappa = 8*g16 + i  <->  token kk*32 + (i < 4 ? 4*g16 + i
-            //            : 16 + 4*g16 + i - 4), i.e. blocks 2kk and 2kk+1 of the S^T accumulators
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float p = (s[tb][r] == -INFINITY) ? 0.f : exp2f(s[tb][r] - m_ref);
+                    s[tb][r] = p;
+                    psum += p;
+                }
+            l_run += psum;
+
+            // ---- O^T += V^T P^T over the tile's 32 tokens
+            // B operand: P^T[kappa][head], kappa = 8*g16 + i  <->  token (i < 4 ? 4*g16 + i
+            //            : 16 + 4*g16 + i - 4), i.e. blocks 0 and 1 of the S^T accumulators
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p0 = (e < 2) ? s[2 * kk][2 * e] : s[2 * kk + 1][2 * e - 4];
-                const float p1 = (e < 2) ? s[2 * kk][2 * e + 1] : s[2 * kk + 1][2 * e - 3];
+                const float p0 = s[e >> 1][2 * (e & 1)];
+                const float p1 = s[e >> 1][2 * (e & 1) + 1];
                 const uint32_t u0 = __float_as_uint(p0) & 0xffff0000u;
                 const uint32_t u1 = __float_as_uint(p1) & 0xffff0000u;
-                const float r0 = p0 - __uint_as_float(u0), r1 = p1 - __uint_as_float(u1);
                 // remainders rounded to nearest bf16
-                const uint32_t v0 = __float_as_uint(r0), v1 = __float_as_uint(r1);
+                const uint32_t v0 = __float_as_uint(p0 - __uint_as_float(u0));
+                const uint32_t v1 = __float_as_uint(p1 - __uint_as_float(u1));
                 const uint32_t w0 = (v0 + 0x7fffu + ((v0 >> 16) & 1u)) >> 16;
                 const uint32_t w1 = (v1 + 0x7fffu + ((v1 >> 16) & 1u)) >> 16;
                 hi[e] = (u0 >> 16) | u1;
@@ -220,21 +312,46 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
             }
             const bf16x8 phi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
             const bf16x8 plo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-            // A operand: V^T[d][kappa] via the transpose load.  In each 16-lane group, lane i
-            // points at row k0 + i/4, dims n0 + 4*(i%4); lane j receives rows k0..k0+3 of dim n0+j.
-            const int rbase0 = kk * 32 + 4 * g16 + (j16 >> 2);
-            const int rbase1 = rbase0 + 16;
-            const int cofs = 4 * (j16 & 3);
+            // A operand: V^T[d][kappa] via the transpose load: in each 16-lane group, lane i
+            // points at row k0 + i/4, dims n0 + 4*(i%4) .. +3; lane j receives rows k0..k0+3 of
+            // dim n0 + j.  Groups of 4 output blocks: group g+1 is read while group g's MFMAs
+            // issue (fenced so the compiler keeps the two-stage ring).
+            bf16x8 va[2][4];
+            auto pv_read = [&](int db0, bf16x8 (&dst)[4]) {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int col = db * 16 + cofs;
-                const uint2 w0 = lds_read_tr16(tile + rbase0 * G::kRowBytes + col * 2);
-                const uint2 w1 = lds_read_tr16(tile + rbase1 * G::kRowBytes + col * 2);
-                const bf16x8 va = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
-                acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[db], 0, 0, 0);
-                acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[db], 0, 0, 0);
+                for (int u = 0; u < 4; ++u) {
+                    const int db = db0 + u;
+                    const unsigned char* p0 = tile + pv_off[db & 7] + (db >> 3) * 256;
+                    const uint2 w0 = lds_read_tr16(p0);
+                    const uint2 w1 = lds_read_tr16(p0 + 16 * G::kRowBytesA);
+                    dst[u] = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+                }
+            };
+            pv_read(0, va[0]);
+#pragma unroll
+            for (int g = 0; g < DB / 4; ++g) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (g + 1 < DB / 4) pv_read(4 * (g + 1), va[(g + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    acc[4 * g + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[g & 1][u], phi, acc[4 * g + u], 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    acc[4 * g + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[g & 1][u], plo, acc[4 * g + u], 0, 0, 0);
             }
         }
+        wait_vm<0>();
+        __syncthreads();                 // a flag raised on the last tile is visible
+        if (*flag == 0) break;           // uniform
+        // second pass with the true max as the reference
+        m_ref = m_seen;
+        l_run = 0.f;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        __syncthreads();                 // everyone has read the flag
+        if (tid == 0) *flag = 0;
+        __syncthreads();
     }
 
     // full row sum of head h0 + j16 across the four lane groups
@@ -259,7 +376,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
                 make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
         if (g16 == 0) {
             // natural-log units, as the combine expects
-            a.part_ml[pidx * 2] = m_run == -INFINITY ? -INFINITY : m_run * 0.6931471805599453f;
+            a.part_ml[pidx * 2] = m_ref == -INFINITY ? -INFINITY : m_ref * 0.6931471805599453f;
             a.part_ml[pidx * 2 + 1] = l_tot;
         }
     }
@@ -267,22 +384,21 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
 
 template <int DK, int DV>
 size_t mfma_smem(int chunk) {
-    return 2 * size_t(Geo<DK>::kTileBytes) + size_t(chunk) * sizeof(int32_t);
+    return size_t(kRing) * Geo<DK, DV>::kTileBytes + size_t(chunk + 4) * sizeof(int32_t);
 }
 
 }  // namespace
 
 namespace tsa {
 
-// Shapes the latent kernel handles: values alias the keys, 64 query heads per KV head group,
-// the 576 / 512 latent widths.
+// Shapes the latent kernel handles: values alias the keys, 64 query heads over one latent KV
+// head of 576 dims whose first 512 are the values.
 bool mfma_latent_applicable(const tsa_kv_pool& pool, const tsa_decode_params& p) {
     const tsa_pool_desc& d = pool.d;
-    if (!d.v_from_k || d.head_dim_k != 576 || d.head_dim_v != 512) return false;
-    if (p.num_q_heads % d.num_kv_heads) return false;
+    if (!d.v_from_k || d.head_dim_k != 576 || d.head_dim_v != 512 || d.num_kv_heads != 1) return false;
+    if (p.num_q_heads != 64) return false;
     if (pool.slots() >= (int64_t(1) << 31)) return false;   // slots kept as 32-bit in LDS
-    if (mfma_smem<576, 512>(int(ceil_div(p.top_k, kTile)) * kTile) > 160 * 1024) return false;
-    return p.num_q_heads / d.num_kv_heads == 64 && d.num_kv_heads == 1;
+    return mfma_smem<576, 512>(int(ceil_div(p.top_k, kTile)) * kTile) <= 160 * 1024;
 }
 
 int mfma_latent_chunk(const tsa_decode_params& p, int* splits) {

@@ -89,6 +89,27 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// max over lanes l, l^16, l^32, l^48 (the four 16-lane groups), with the cross-half swaps
+__device__ __forceinline__ float max4groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum4groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// two floats rounded to nearest-even bf16, packed (first in the low half)
+__device__ __forceinline__ uint32_t pack_bf16(float x, float y) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+    const bf16x2 v = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // LDS transpose load of 4 x 16-bit.  In each 16-lane group, lane i supplies the address of 4
 // consecutive elements; lane j receives element j%4 of the data addressed by lanes
 // j/4, 4 + j/4, 8 + j/4, 12 + j/4.
@@ -219,127 +240,145 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
     // the split is then computed again with m_ref = that max.  Inputs whose logits stay within
     // 2^32 of the first tile's max take one pass.
     float m_seen = -INFINITY;  // max logit (log2 units) over the tiles scanned so far
+
+    // S^T = K Q^T for one tile: two 16-token blocks x 16 heads.  Operand reads run kQkAhead
+    // k-steps ahead of the MFMAs (a register ring); the scheduling fences keep the compiler from
+    // sinking the reads next to their use.
+    auto qk_tile = [&](const unsigned char* tile, f32x4 (&s)[2]) {
+        s[0] = s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        uint4 kv[kQkAhead][2];
+        auto qk_read = [&](int ks, uint4 (&dst)[2]) {
+            const unsigned char* base = ks < KSA ? tile + qk_off[ks & 3] + (ks >> 2) * 256
+                                                 : tile + qkb_off[ks - KSA];
+            const int second = ks < KSA ? 16 * G::kRowBytesA : 16 * G::kRowBytesB;
+            dst[0] = *reinterpret_cast<const uint4*>(base);
+            dst[1] = *reinterpret_cast<const uint4*>(base + second);
+        };
+#pragma unroll
+        for (int ks = 0; ks < kQkAhead; ++ks) qk_read(ks, kv[ks]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8 qb = as_bf16x8(qreg[ks]);
+            s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks % kQkAhead][0]), qb, s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks % kQkAhead][1]), qb, s[1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + kQkAhead < KS) qk_read(ks + kQkAhead, kv[ks % kQkAhead]);
+        }
+    };
+
+    // O^T += V^T P^T over one tile's 32 tokens.  A operand: V^T[d][kappa] via the transpose
+    // load (in each 16-lane group, lane i points at row k0 + i/4, dims n0 + 4*(i%4) .. +3; lane j
+    // receives rows k0..k0+3 of dim n0 + j).  Groups of 4 output blocks: group g+1 is read while
+    // group g's MFMAs issue (fenced so the compiler keeps the two-stage ring).
+    auto pv_tile = [&](const unsigned char* tile, const bf16x8& phi, const bf16x8& plo) {
+        bf16x8 va[2][4];
+        auto pv_read = [&](int db0, bf16x8 (&dst)[4]) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int db = db0 + u;
+                const unsigned char* p0 = tile + pv_off[db & 7] + (db >> 3) * 256;
+                const uint2 w0 = lds_read_tr16(p0);
+                const uint2 w1 = lds_read_tr16(p0 + 16 * G::kRowBytesA);
+                dst[u] = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+            }
+        };
+        pv_read(0, va[0]);
+#pragma unroll
+        for (int g = 0; g < DB / 4; ++g) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (g + 1 < DB / 4) pv_read(4 * (g + 1), va[(g + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                acc[4 * g + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[g & 1][u], phi, acc[4 * g + u], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                acc[4 * g + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[g & 1][u], plo, acc[4 * g + u], 0, 0, 0);
+        }
+    };
+
+    // Softmax reference: the probabilities are exp2(logit - m_ref) with m_ref fixed at the first
+    // tile where the head has a valid token, never rescaled.  Any reference gives the same
+    // softmax as long as exp2 cannot overflow, so a tile whose max exceeds m_ref by more than
+    // kHeadroom (2^32) switches the whole workgroup to a scan that only tracks the true max;
+    // the split is then computed again with m_ref = that max.  Inputs whose logits stay within
+    // 2^32 of the first tile's max take one pass.
+    //
+    // Order inside the loop: the QK MFMAs of tile t+1 are issued before the softmax of tile t,
+    // so the matrix cores work while the vector ALUs compute probabilities; then PV of tile t.
     for (int pass = 0; pass < 2; ++pass) {
         bool scan = false;
+        f32x4 s_cur[2], s_next[2];
+        uint64_t live_cur = 0, live_next = 0;
+        auto live_mask = [&](int t) {
+            return __ballot(lane < kTile && t * kTile + lane < n &&
+                            rows[t * kTile + (lane & (kTile - 1))] >= 0);
+        };
         if (n_tiles > 0) issue_tile(0);
         if (n_tiles > 1) issue_tile(1);
         if (n_tiles > 2) issue_tile(2);
-        for (int t = 0; t < n_tiles; ++t) {
-            // tile t has landed once at most the loads of tiles t+1, t+2 are still outstanding
-            if (t + 2 < n_tiles) wait_vm<2 * kLoadsPerWave>();
-            else if (t + 1 < n_tiles) wait_vm<kLoadsPerWave>();
+        if (n_tiles > 0) {
+            if (n_tiles > 2) wait_vm<2 * kLoadsPerWave>();
+            else if (n_tiles > 1) wait_vm<kLoadsPerWave>();
             else wait_vm<0>();
-            __syncthreads();   // every wave's part landed; tile t-1's buffer is free again
-            scan = *flag != 0;
-            if (t + 3 < n_tiles) issue_tile(t + 3);
+            __syncthreads();
+            live_cur = live_mask(0);
+            qk_tile(ring, s_cur);
+        }
+        for (int t = 0; t < n_tiles; ++t) {
+            if (t + 1 < n_tiles) {
+                // tile t+1 has landed once at most tile t+2's loads are outstanding
+                if (t + 2 < n_tiles) wait_vm<kLoadsPerWave>();
+                else wait_vm<0>();
+                __syncthreads();   // every wave's part landed; tile t-1's buffer is free again
+                scan = *flag != 0;
+                if (t + 3 < n_tiles) issue_tile(t + 3);
+                live_next = live_mask(t + 1);
+                qk_tile(ring + ((t + 1) % kRing) * G::kTileBytes, s_next);
+            }
             const unsigned char* tile = ring + (t % kRing) * G::kTileBytes;
 
-            // ---- S^T = K Q^T : two 16-token blocks x 16 heads
-            f32x4 s[2];
-            s[0] = s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-            {
-                // operand reads run kQkAhead k-steps ahead of the MFMAs (a register ring); the
-                // scheduling fences keep the compiler from sinking the reads next to their use
-                uint4 kv[kQkAhead][2];
-                auto qk_read = [&](int ks, uint4 (&dst)[2]) {
-                    const unsigned char* base = ks < KSA ? tile + qk_off[ks & 3] + (ks >> 2) * 256
-                                                         : tile + qkb_off[ks - KSA];
-                    const int second = ks < KSA ? 16 * G::kRowBytesA : 16 * G::kRowBytesB;
-                    dst[0] = *reinterpret_cast<const uint4*>(base);
-                    dst[1] = *reinterpret_cast<const uint4*>(base + second);
-                };
-#pragma unroll
-                for (int ks = 0; ks < kQkAhead; ++ks) qk_read(ks, kv[ks]);
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    const bf16x8 qb = as_bf16x8(qreg[ks]);
-                    s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks % kQkAhead][0]), qb, s[0], 0, 0, 0);
-                    s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks % kQkAhead][1]), qb, s[1], 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (ks + kQkAhead < KS) qk_read(ks + kQkAhead, kv[ks % kQkAhead]);
-                }
-            }
-            // lane holds S^T[token tb*16 + 4*g16 + r][head h0 + j16]; bit j of `live` = token j
-            // of the tile is a selected, resolvable row
-            const uint64_t live = __ballot(lane < kTile && t * kTile + lane < n &&
-                                           rows[t * kTile + (lane & (kTile - 1))] >= 0);
+            // lane holds S^T[token tb*16 + 4*g16 + r][head h0 + j16]
             float tmax = -INFINITY;
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int tok = tb * 16 + g16 * 4 + r;
-                    const float x = ((live >> tok) & 1) ? s[tb][r] * a.scale_log2 : -INFINITY;
-                    s[tb][r] = x;
+                    const float x = ((live_cur >> tok) & 1) ? s_cur[tb][r] * a.scale_log2 : -INFINITY;
+                    s_cur[tb][r] = x;
                     tmax = fmaxf(tmax, x);
                 }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            tmax = max4groups(tmax);
             m_seen = fmaxf(m_seen, tmax);
-            if (scan) continue;                      // uniform: the flag was read after a barrier
-            if (m_ref == -INFINITY) m_ref = tmax;    // first tile with a valid token for the head
-            if (__ballot(tmax > m_ref + kHeadroom)) *flag = 1;
-
-            float psum = 0.f;
+            if (!scan) {                             // uniform: the flag was read after a barrier
+                if (m_ref == -INFINITY) m_ref = tmax;    // first tile with a valid token for the head
+                if (__ballot(tmax > m_ref + kHeadroom)) *flag = 1;
+                float p[8];
+                float psum = 0.f;
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = (s[tb][r] == -INFINITY) ? 0.f : exp2f(s[tb][r] - m_ref);
-                    s[tb][r] = p;
-                    psum += p;
+                for (int i = 0; i < 8; ++i) {
+                    const float x = s_cur[i >> 2][i & 3];
+                    p[i] = (x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x - m_ref);
+                    psum += p[i];
                 }
-            l_run += psum;
-
-            // ---- O^T += V^T P^T over the tile's 32 tokens
-            // B operand: P^T[kappa][head], kappa = 8*g16 + i  <->  token (i < 4 ? 4*g16 + i
-            //            : 16 + 4*g16 + i - 4), i.e. blocks 0 and 1 of the S^T accumulators
-            uint32_t hi[4], lo[4];
+                l_run += psum;
+                // B operand: P^T[kappa][head], kappa = 8*g16 + i  <->  token (i < 4 ? 4*g16 + i
+                // : 16 + 4*g16 + i - 4), i.e. p[i] in order; split into bf16 hi + lo
+                uint32_t hi[4], lo[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p0 = s[e >> 1][2 * (e & 1)];
-                const float p1 = s[e >> 1][2 * (e & 1) + 1];
-                const uint32_t u0 = __float_as_uint(p0) & 0xffff0000u;
-                const uint32_t u1 = __float_as_uint(p1) & 0xffff0000u;
-                // remainders rounded to nearest bf16
-                const uint32_t v0 = __float_as_uint(p0 - __uint_as_float(u0));
-                const uint32_t v1 = __float_as_uint(p1 - __uint_as_float(u1));
-                const uint32_t w0 = (v0 + 0x7fffu + ((v0 >> 16) & 1u)) >> 16;
-                const uint32_t w1 = (v1 + 0x7fffu + ((v1 >> 16) & 1u)) >> 16;
-                hi[e] = (u0 >> 16) | u1;
-                lo[e] = w0 | (w1 << 16);
-            }
-            const bf16x8 phi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-            const bf16x8 plo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-            // A operand: V^T[d][kappa] via the transpose load: in each 16-lane group, lane i
-            // points at row k0 + i/4, dims n0 + 4*(i%4) .. +3; lane j receives rows k0..k0+3 of
-            // dim n0 + j.  Groups of 4 output blocks: group g+1 is read while group g's MFMAs
-            // issue (fenced so the compiler keeps the two-stage ring).
-            bf16x8 va[2][4];
-            auto pv_read = [&](int db0, bf16x8 (&dst)[4]) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int db = db0 + u;
-                    const unsigned char* p0 = tile + pv_off[db & 7] + (db >> 3) * 256;
-                    const uint2 w0 = lds_read_tr16(p0);
-                    const uint2 w1 = lds_read_tr16(p0 + 16 * G::kRowBytesA);
-                    dst[u] = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+                for (int e = 0; e < 4; ++e) {
+                    hi[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
+                    lo[e] = pack_bf16(p[2 * e] - __uint_as_float(hi[e] << 16),
+                                      p[2 * e + 1] - __uint_as_float(hi[e] & 0xffff0000u));
                 }
-            };
-            pv_read(0, va[0]);
-#pragma unroll
-            for (int g = 0; g < DB / 4; ++g) {
-                __builtin_amdgcn_sched_barrier(0);
-                if (g + 1 < DB / 4) pv_read(4 * (g + 1), va[(g + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    acc[4 * g + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[g & 1][u], phi, acc[4 * g + u], 0, 0, 0);
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    acc[4 * g + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[g & 1][u], plo, acc[4 * g + u], 0, 0, 0);
+                pv_tile(tile, as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3])),
+                        as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3])));
             }
+            s_cur[0] = s_next[0];
+            s_cur[1] = s_next[1];
+            live_cur = live_next;
         }
         wait_vm<0>();
         __syncthreads();                 // a flag raised on the last tile is visible
@@ -355,9 +394,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
     }
 
     // full row sum of head h0 + j16 across the four lane groups
-    float l_tot = l_run;
-    l_tot += __shfl_xor(l_tot, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = sum4groups(l_run);
     const int h = h0 + j16;
     // lane holds O^T[d = db*16 + 4*g16 + r][head h]
     if (a.splits == 1) {

@@ -108,6 +108,209 @@ __global__ void __launch_bounds__(kThreads) indexer_score_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Single-head indexer (the common case): every wave streams its own run of tokens through a
+// private ring of LDS slots with global-to-LDS loads, which sustain more HBM bandwidth than
+// loads into registers.  A slot holds 16 token rows; lane (j16, g16) dots row j16's quarter
+// g16 with the matching quarter of the query, and the four quarters are summed with the
+// cross-half lane swaps.  Rows are stored with their 16-byte chunks XOR-swizzled so that the
+// 16 rows read in parallel fall on distinct LDS banks.
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+constexpr int kRing = 4;              // slots per wave
+constexpr int kUnit = 16;             // tokens per slot
+constexpr int kMaxTpw = 4096;         // tokens per wave at most
+constexpr int kMinPage = 16;          // smallest page size this kernel takes
+constexpr int kPagesPerWave = kMaxTpw / kMinPage + 2;
+
+__device__ __forceinline__ void load_lds16(const void* gsrc, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gsrc), "s"(lds)
+                 : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ float sum4groups(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+template <int D>
+struct IdxGeo {
+    static constexpr int kRowBytes = 2 * D;
+    static constexpr int kCpr = D / 8;                    // 16-byte chunks per row
+    static constexpr int kSlotBytes = kUnit * kRowBytes;
+    static constexpr int kLoads = kSlotBytes / 1024;      // wave-wide loads per slot
+    static constexpr int kPart = D / 4;                   // dims per lane
+    static constexpr int kPartChunks = kPart / 8;
+    static constexpr int kRowsPer256 = 256 / kRowBytes > 0 ? 256 / kRowBytes : 1;
+    static_assert(kSlotBytes % 1024 == 0, "a slot is a whole number of wave loads");
+};
+
+// stored chunk position of logical chunk c of slot row r
+template <int D>
+__device__ __forceinline__ int idx_swz(int r, int c) {
+    using G = IdxGeo<D>;
+    const int m = G::kCpr < 16 ? G::kCpr - 1 : 15;
+    return c ^ ((r / G::kRowsPer256) & m);
+}
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// ALIGNED: page_size is a power of two and a multiple of the 16-token slot, so every slot lies in
+// one page and the page id is the same for the whole wave.
+template <int D, bool ALIGNED>
+__global__ void __launch_bounds__(256) indexer_score_lds_kernel(
+    const uint16_t* __restrict__ qidx, const float* __restrict__ widx,
+    const int32_t* __restrict__ page_table, int max_pages, int page_size, int page_shift,
+    int num_pages, const int32_t* __restrict__ seq_lens, int max_len,
+    const uint16_t* __restrict__ kpool, float* __restrict__ scores, int ld, int tok_per_wave) {
+    using G = IdxGeo<D>;
+    __shared__ __align__(16) unsigned char ring[4][kRing][G::kSlotBytes];
+    __shared__ int32_t wpages[4][kPagesPerWave];   // page ids of each wave's token run
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j16 = lane & 15, g16 = lane >> 4;
+    int len = seq_lens[b];
+    len = len < 0 ? 0 : (len > max_len ? max_len : len);
+    const int t0 = (blockIdx.x * 4 + wave) * tok_per_wave;
+    const int t1 = min(t0 + tok_per_wave, len);
+    if (t0 >= t1) return;
+    const int n_units = (t1 - t0 + kUnit - 1) / kUnit;
+    const int32_t* pt = page_table + int64_t(b) * max_pages;
+    // the run's page ids, staged once so that load addresses do not wait on the page table
+    const int pg0 = ALIGNED ? (t0 >> page_shift) : t0 / page_size;
+    const int pg1 = ALIGNED ? ((t1 - 1) >> page_shift) : (t1 - 1) / page_size;
+    int32_t* wp = wpages[wave];
+    for (int i = lane; i <= pg1 - pg0; i += 64) {
+        const int32_t pid = pt[pg0 + i];
+        wp[i] = (pid >= 0 && pid < num_pages) ? pid : -1;
+    }
+
+    // query quarter g16 of this lane, as bf16 pairs
+    uint32_t q[G::kPart / 2];
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(qidx + int64_t(b) * D + g16 * G::kPart);
+#pragma unroll
+        for (int c = 0; c < G::kPartChunks; ++c) {
+            const uint4 v = src[c];
+            q[4 * c + 0] = v.x; q[4 * c + 1] = v.y; q[4 * c + 2] = v.z; q[4 * c + 3] = v.w;
+        }
+    }
+    const float w = widx[0];
+    wait_vm<0>();
+
+    const uint32_t ring_base = uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)(&ring[wave][0][0])));
+    // load k of a slot fills stored chunks 64 k .. 64 k + 63 (row-major); each lane fetches the
+    // logical chunk that belongs at its stored position
+    int lrow[G::kLoads], lsrc[G::kLoads];   // lane constants: slot row, element offset in the row
+#pragma unroll
+    for (int k = 0; k < G::kLoads; ++k) {
+        const int pc = k * 64 + lane;
+        lrow[k] = pc / G::kCpr;
+        lsrc[k] = idx_swz<D>(lrow[k], pc % G::kCpr) * 8;
+    }
+    auto issue = [&](int u) {
+        const uint32_t slot = ring_base + uint32_t((u % kRing) * G::kSlotBytes);
+        const int tu = t0 + u * kUnit;
+        if (ALIGNED) {
+            // one page for the slot; rows past the run re-read the slot's first row
+            const int page = __builtin_amdgcn_readfirstlane(wp[(tu >> page_shift) - pg0]);
+            const int64_t row0 = int64_t(page < 0 ? 0 : page) * page_size + (tu & (page_size - 1));
+#pragma unroll
+            for (int k = 0; k < G::kLoads; ++k) {
+                const int r = tu + lrow[k] < t1 ? lrow[k] : 0;
+                load_lds16(kpool + (row0 + r) * D + lsrc[k],
+                           __builtin_amdgcn_readfirstlane(slot + uint32_t(k * 1024)));
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < G::kLoads; ++k) {
+                const int t = tu + lrow[k];
+                int page = -1, off = 0;
+                if (t < t1) {
+                    page = wp[t / page_size - pg0];
+                    off = t % page_size;
+                }
+                const uint16_t* src = kpool + (page >= 0 ? (int64_t(page) * page_size + off) * D + lsrc[k] : 0);
+                load_lds16(src, __builtin_amdgcn_readfirstlane(slot + uint32_t(k * 1024)));
+            }
+        }
+    };
+    for (int u = 0; u < kRing - 1 && u < n_units; ++u) issue(u);
+
+    const int rd_row = j16 * G::kRowBytes;
+    int rd_off[G::kPartChunks];
+#pragma unroll
+    for (int c = 0; c < G::kPartChunks; ++c) rd_off[c] = rd_row + idx_swz<D>(j16, g16 * G::kPartChunks + c) * 16;
+
+    for (int u = 0; u < n_units; ++u) {
+        if (u + kRing - 1 < n_units) {
+            issue(u + kRing - 1);
+            wait_vm<(kRing - 1) * G::kLoads>();
+        } else if (u + 2 < n_units) {
+            wait_vm<2 * G::kLoads>();
+        } else if (u + 1 < n_units) {
+            wait_vm<G::kLoads>();
+        } else {
+            wait_vm<0>();
+        }
+        const unsigned char* slot = &ring[wave][u % kRing][0];
+        float d = 0.f;
+#pragma unroll
+        for (int c = 0; c < G::kPartChunks; ++c) {
+            const uint4 v = *reinterpret_cast<const uint4*>(slot + rd_off[c]);
+            d = dot2(q[4 * c + 0], v.x, d);
+            d = dot2(q[4 * c + 1], v.y, d);
+            d = dot2(q[4 * c + 2], v.z, d);
+            d = dot2(q[4 * c + 3], v.w, d);
+        }
+        d = sum4groups(d);
+        const int t = t0 + u * kUnit + j16;
+        if (g16 == 0 && t < t1) {
+            const int page = ALIGNED ? wp[(t >> page_shift) - pg0] : wp[t / page_size - pg0];
+            scores[int64_t(b) * ld + t] = page >= 0 ? w * fmaxf(d, 0.f) : -INFINITY;
+        }
+    }
+}
+
+template <int D>
+hipError_t launch_lds(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
+                      const void* qidx, const float* widx, const int32_t* page_table,
+                      int max_pages, const int32_t* seq_lens, float* scores, int ld,
+                      hipStream_t s, int shift) {
+    const tsa_pool_desc& d = pool.d;
+    // about 2048 waves over the whole batch (8 per CU), at least a few slots each
+    const int64_t total = int64_t(p.batch) * p.max_len;
+    int tpw = int((total + 2047) / 2048);
+    tpw = std::max(kUnit * 4, std::min(tpw, kMaxTpw));
+    tpw = (tpw + kUnit - 1) / kUnit * kUnit;
+    dim3 grid((p.max_len + 4 * tpw - 1) / (4 * tpw), p.batch);
+    const uint16_t* kpool = static_cast<const uint16_t*>(pool.idx) + int64_t(layer) * pool.slots() * D;
+    const bool aligned = shift >= 0 && d.page_size % kUnit == 0;
+    if (aligned)
+        hipLaunchKernelGGL((indexer_score_lds_kernel<D, true>), grid, dim3(256), 0, s,
+                           static_cast<const uint16_t*>(qidx), widx, page_table, max_pages, d.page_size,
+                           shift, d.num_pages, seq_lens, p.max_len, kpool, scores, ld, tpw);
+    else
+        hipLaunchKernelGGL((indexer_score_lds_kernel<D, false>), grid, dim3(256), 0, s,
+                           static_cast<const uint16_t*>(qidx), widx, page_table, max_pages, d.page_size,
+                           shift, d.num_pages, seq_lens, p.max_len, kpool, scores, ld, tpw);
+    return hipGetLastError();
+}
+
 template <int LPT>
 hipError_t launch_lpt(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                       const void* qidx, const float* widx, const int32_t* page_table,
@@ -144,6 +347,20 @@ hipError_t launch_indexer_scores(const tsa_kv_pool& pool, int layer, const tsa_d
                                  const void* qidx, const float* widx, const int32_t* page_table,
                                  int max_pages, const int32_t* seq_lens, float* scores, int ld,
                                  hipStream_t s) {
+    if (p.index_heads == 1 && pool.d.page_size >= kMinPage) {
+        int shift = -1;
+        if ((pool.d.page_size & (pool.d.page_size - 1)) == 0) {
+            shift = 0;
+            while ((1 << shift) < pool.d.page_size) ++shift;
+        }
+        switch (pool.d.index_dim) {
+            case 32: return launch_lds<32>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
+            case 64: return launch_lds<64>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
+            case 128: return launch_lds<128>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
+            case 256: return launch_lds<256>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
+            default: break;
+        }
+    }
     switch (pool.d.index_dim / 8) {
         case 1: return launch_lpt<1>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s);
         case 2: return launch_lpt<2>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s);

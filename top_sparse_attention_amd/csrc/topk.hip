@@ -6,8 +6,11 @@
 //
 // Method: scores map to order-preserving 32-bit keys.  Four 8-bit radix passes narrow the key
 // of the k-th largest element (a histogram of the candidate digits per pass, kept in LDS as 16
-// interleaved copies so that lanes hitting the same bin spread over distinct addresses).  After
-// the passes, every element whose key exceeds the threshold is kept, and of the elements equal
+// interleaved copies so that lanes hitting the same bin spread over distinct addresses).  A pass
+// also finds the smallest and largest candidate key; when they are equal the threshold key is
+// known and the remaining passes are skipped (ties at the threshold are common for
+// integer-valued scores).  After the passes, every element whose key exceeds the threshold is
+// kept, and of the elements equal
 // to it the lowest positions fill the rest; a block-wide scan over positions (each thread
 // owns a contiguous run of positions) yields both the tie ranks and the output offsets, so the
 // output comes out ascending with no sort.
@@ -62,6 +65,7 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
     __shared__ uint32_t hist[256 * kCopies];
     __shared__ int sh_scan[2 * kWaves + 1];
     __shared__ int sh_sel[4];
+    __shared__ uint32_t sh_mm[2];
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
@@ -75,21 +79,63 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
     const float* s = scores + int64_t(b) * ld;
     const int base = tid * IPT;
     uint32_t key[IPT];
+    if (IPT >= 4 && (ld & 3) == 0) {
 #pragma unroll
-    for (int i = 0; i < IPT; ++i) key[i] = (base + i < len) ? order_key(s[base + i]) : 0u;
+        for (int i = 0; i < IPT; i += 4) {
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (base + i + 3 < len) {
+                v = *reinterpret_cast<const float4*>(s + base + i);
+            } else {
+                if (base + i < len) v.x = s[base + i];
+                if (base + i + 1 < len) v.y = s[base + i + 1];
+                if (base + i + 2 < len) v.z = s[base + i + 2];
+            }
+            key[i] = order_key(v.x);
+            key[i + 1] = order_key(v.y);
+            key[i + 2] = order_key(v.z);
+            key[i + 3] = order_key(v.w);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) key[i] = (base + i < len) ? order_key(s[base + i]) : 0u;
+    }
 
     uint32_t prefix = 0, mask = 0;
     int remaining = k;  // how many of the elements matching `prefix` under `mask` to keep
     for (int shift = 24; shift >= 0; shift -= 8) {
         for (int i = tid; i < 256 * kCopies; i += kThreads) hist[i] = 0;
-        __syncthreads();
-        const int copy = tid & (kCopies - 1);
-#pragma unroll
-        for (int i = 0; i < IPT; ++i) {
-            if (base + i < len && (key[i] & mask) == prefix)
-                atomicAdd(&hist[((key[i] >> shift) & 255u) * kCopies + copy], 1u);
+        if (tid == 0) {
+            sh_mm[0] = 0xffffffffu;
+            sh_mm[1] = 0u;
         }
         __syncthreads();
+        const int copy = tid & (kCopies - 1);
+        uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+        for (int i = 0; i < IPT; ++i) {
+            if (base + i < len && (key[i] & mask) == prefix) {
+                atomicAdd(&hist[((key[i] >> shift) & 255u) * kCopies + copy], 1u);
+                kmin = min(kmin, key[i]);
+                kmax = max(kmax, key[i]);
+            }
+        }
+        // candidates' key range: once they are all equal, the k-th key is known exactly
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+            kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+        }
+        if ((tid & 63) == 0) {
+            atomicMin(&sh_mm[0], kmin);
+            atomicMax(&sh_mm[1], kmax);
+        }
+        __syncthreads();
+        if (sh_mm[0] == sh_mm[1]) {      // uniform
+            prefix = sh_mm[0];
+            mask = 0xffffffffu;
+            __syncthreads();
+            break;
+        }
         // bins in descending digit order: thread j < 256 owns digit 255 - j
         int c = 0;
         if (tid < 256) {

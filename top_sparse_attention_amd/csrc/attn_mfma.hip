@@ -241,10 +241,59 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
     // 2^32 of the first tile's max take one pass.
     float m_seen = -INFINITY;  // max logit (log2 units) over the tiles scanned so far
 
+    // Softmax of one tile as a sequence of small stages, so that they can be slotted between
+    // the QK MFMAs of the next tile: the matrix cores work while the vector ALUs run these.
+    // State of the tile being normalised:
+    float sx[8];                 // scaled logits, then probabilities
+    float stmax = -INFINITY, spsum = 0.f;
+    bool sviol = false;
+    uint32_t phi_w[4], plo_w[4];
+    bool scan = false;           // uniform; the workgroup is only tracking the max
+    auto soft_stage = [&](int st, const f32x4 (&sc)[2], uint64_t live) {
+        if (st == 0 || st == 1) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 4 * st + r;
+                const int tok = st * 16 + g16 * 4 + r;
+                const float x = ((live >> tok) & 1) ? sc[st][r] * a.scale_log2 : -INFINITY;
+                sx[i] = x;
+                stmax = fmaxf(stmax, x);
+            }
+        } else if (st == 2) {
+            stmax = max4groups(stmax);
+            m_seen = fmaxf(m_seen, stmax);
+            if (m_ref == -INFINITY) m_ref = stmax;   // first tile with a valid token for the head
+            sviol = stmax > m_ref + kHeadroom;
+        } else if (st == 3) {
+            if (!scan && __ballot(sviol)) *flag = 1;
+        } else if (st >= 4 && st < 8) {
+            const int i = 2 * (st - 4);
+            sx[i] = (sx[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sx[i] - m_ref);
+            sx[i + 1] = (sx[i + 1] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sx[i + 1] - m_ref);
+            spsum += sx[i] + sx[i + 1];
+        } else if (st >= 8 && st < 12) {
+            // B operand of PV: P^T[kappa][head], kappa = 8*g16 + i <-> token (i < 4 ? 4*g16 + i :
+            // 16 + 4*g16 + i - 4), i.e. sx[i] in order; split into bf16 hi + lo
+            const int e = st - 8;
+            const uint32_t h = pack_bf16(sx[2 * e], sx[2 * e + 1]);
+            phi_w[e] = h;
+            plo_w[e] = pack_bf16(sx[2 * e] - __uint_as_float(h << 16),
+                                 sx[2 * e + 1] - __uint_as_float(h & 0xffff0000u));
+        }
+    };
+    constexpr int kStages = 12;
+    auto soft_reset = [&]() {
+        stmax = -INFINITY;
+        spsum = 0.f;
+        sviol = false;
+    };
+
     // S^T = K Q^T for one tile: two 16-token blocks x 16 heads.  Operand reads run kQkAhead
-    // k-steps ahead of the MFMAs (a register ring); the scheduling fences keep the compiler from
-    // sinking the reads next to their use.
-    auto qk_tile = [&](const unsigned char* tile, f32x4 (&s)[2]) {
+    // k-steps ahead of the MFMAs (a register ring).  When `prev` is set, softmax stage ks of the
+    // previous tile runs after the MFMAs of k-step ks.  The scheduling fences keep the compiler
+    // from regrouping the pieces.
+    auto qk_tile = [&](const unsigned char* tile, f32x4 (&s)[2], bool with_soft,
+                       const f32x4 (&sc)[2], uint64_t live) {
         s[0] = s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
         uint4 kv[kQkAhead][2];
         auto qk_read = [&](int ks, uint4 (&dst)[2]) {
@@ -262,6 +311,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
             const bf16x8 qb = as_bf16x8(qreg[ks]);
             s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks % kQkAhead][0]), qb, s[0], 0, 0, 0);
             s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks % kQkAhead][1]), qb, s[1], 0, 0, 0);
+            if (with_soft && ks < kStages) soft_stage(ks, sc, live);
             __builtin_amdgcn_sched_barrier(0);
             if (ks + kQkAhead < KS) qk_read(ks + kQkAhead, kv[ks % kQkAhead]);
         }
@@ -305,10 +355,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
     // the split is then computed again with m_ref = that max.  Inputs whose logits stay within
     // 2^32 of the first tile's max take one pass.
     //
-    // Order inside the loop: the QK MFMAs of tile t+1 are issued before the softmax of tile t,
-    // so the matrix cores work while the vector ALUs compute probabilities; then PV of tile t.
+    // Loop body for tile t: QK of tile t+1 (with tile t's softmax stages in its shadow), then PV
+    // of tile t.
     for (int pass = 0; pass < 2; ++pass) {
-        bool scan = false;
+        scan = false;
         f32x4 s_cur[2], s_next[2];
         uint64_t live_cur = 0, live_next = 0;
         auto live_mask = [&](int t) {
@@ -324,9 +374,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
             else wait_vm<0>();
             __syncthreads();
             live_cur = live_mask(0);
-            qk_tile(ring, s_cur);
+            qk_tile(ring, s_cur, false, s_cur, 0);
         }
         for (int t = 0; t < n_tiles; ++t) {
+            soft_reset();
             if (t + 1 < n_tiles) {
                 // tile t+1 has landed once at most tile t+2's loads are outstanding
                 if (t + 2 < n_tiles) wait_vm<kLoadsPerWave>();
@@ -335,46 +386,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
                 scan = *flag != 0;
                 if (t + 3 < n_tiles) issue_tile(t + 3);
                 live_next = live_mask(t + 1);
-                qk_tile(ring + ((t + 1) % kRing) * G::kTileBytes, s_next);
+                qk_tile(ring + ((t + 1) % kRing) * G::kTileBytes, s_next, true, s_cur, live_cur);
+            } else {
+#pragma unroll
+                for (int st = 0; st < kStages; ++st) soft_stage(st, s_cur, live_cur);
             }
-            const unsigned char* tile = ring + (t % kRing) * G::kTileBytes;
-
-            // lane holds S^T[token tb*16 + 4*g16 + r][head h0 + j16]
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tok = tb * 16 + g16 * 4 + r;
-                    const float x = ((live_cur >> tok) & 1) ? s_cur[tb][r] * a.scale_log2 : -INFINITY;
-                    s_cur[tb][r] = x;
-                    tmax = fmaxf(tmax, x);
-                }
-            tmax = max4groups(tmax);
-            m_seen = fmaxf(m_seen, tmax);
-            if (!scan) {                             // uniform: the flag was read after a barrier
-                if (m_ref == -INFINITY) m_ref = tmax;    // first tile with a valid token for the head
-                if (__ballot(tmax > m_ref + kHeadroom)) *flag = 1;
-                float p[8];
-                float psum = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float x = s_cur[i >> 2][i & 3];
-                    p[i] = (x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x - m_ref);
-                    psum += p[i];
-                }
-                l_run += psum;
-                // B operand: P^T[kappa][head], kappa = 8*g16 + i  <->  token (i < 4 ? 4*g16 + i
-                // : 16 + 4*g16 + i - 4), i.e. p[i] in order; split into bf16 hi + lo
-                uint32_t hi[4], lo[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    hi[e] = pack_bf16(p[2 * e], p[2 * e + 1]);
-                    lo[e] = pack_bf16(p[2 * e] - __uint_as_float(hi[e] << 16),
-                                      p[2 * e + 1] - __uint_as_float(hi[e] & 0xffff0000u));
-                }
-                pv_tile(tile, as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3])),
-                        as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3])));
+            if (!scan) {
+                l_run += spsum;
+                pv_tile(ring + (t % kRing) * G::kTileBytes,
+                        as_bf16x8(make_uint4(phi_w[0], phi_w[1], phi_w[2], phi_w[3])),
+                        as_bf16x8(make_uint4(plo_w[0], plo_w[1], plo_w[2], plo_w[3])));
             }
             s_cur[0] = s_next[0];
             s_cur[1] = s_next[1];

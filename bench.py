@@ -31,8 +31,12 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 
 
 def _src_hash(name: str) -> str:
+    """Hash of a kernel source's code: comment-only lines and blank lines are left out, so that
+    editing a comment does not disown the counters taken on the same code."""
     p = os.path.join(ROOT, "top_sparse_attention_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    code = [ln.rstrip() for ln in open(p, encoding="utf-8")
+            if ln.strip() and not ln.lstrip().startswith("//")]
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def _traffic(kernel_src: str, key: str):
@@ -65,20 +69,24 @@ def cpu_baseline(w, seed: int, budget_s: float = 15.0):
     qi = synth.index_queries(w, seed)
     q = synth.queries(w, seed)
     wi = synth.index_weights(w)
-    done, spent = 0, 0.0
-    b = 0
+    done, spent, b, passes = 0, 0.0, 0, 0
     while spent < budget_s and b < len(lens):
         L = int(lens[b])
         kidx, kk, vv = synth.request_tokens(w, seed, b, L)
-        t0 = time.perf_counter()
-        decode.request_step(q[b], qi[b], wi, kidx, kk, vv, w.top_k, w.sm_scale,
-                            v_from_k_dims=w.head_dim_v if w.v_from_k else 0)
-        spent += time.perf_counter() - t0
-        done += 1
+        # repeat each request so that one pass over all requests roughly fills the budget
+        reps = 1 if done == 0 else max(1, int(budget_s / max(spent / done, 1e-9) / len(lens)))
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            decode.request_step(q[b], qi[b], wi, kidx, kk, vv, w.top_k, w.sm_scale,
+                                v_from_k_dims=w.head_dim_v if w.v_from_k else 0)
+            spent += time.perf_counter() - t0
+            done += 1
+        passes = max(passes, reps)
         b += 1
     return {"value": done / spent, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"{done} of {len(lens)} requests of {w.name} (full context each), "
-                      f"{spent:.1f} s of oracle time; input generation not timed",
+            "sample": f"{done} request steps over the first {b} of {len(lens)} requests of {w.name} "
+                      f"(full context each, up to {passes} repeats per request), {spent:.1f} s of "
+                      f"oracle time; input generation not timed",
             "cpu": _cpu_model(), "host_cores": len(os.sched_getaffinity(0))}
 
 
@@ -92,6 +100,81 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+CALIB_KERNEL = "bitwise_not"   # torch's elementwise kernel name for the calibration copy
+TRAFFIC_KERNELS = {            # profiles/traffic.json key prefix -> (kernel-name test, source)
+    "indexer_score": (lambda n: "indexer_score" in n, "indexer_score.hip"),
+    "attention": (lambda n: "attn" in n and "combine" not in n, None),
+    "combine": (lambda n: "combine" in n, "attn_valu.hip"),
+    "topk": (lambda n: "topk" in n, "topk.hip"),
+}
+
+
+def copy_calibration(mib: int):
+    """A plain streaming copy of known size (int32 bitwise-not: reads N bytes, writes N bytes),
+    run three times, so that the FETCH_SIZE / WRITE_SIZE counters can be scaled to bytes."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"[bench] calibration copy: {mib} MiB read + {mib} MiB written per launch",
+          file=sys.stderr, flush=True)
+    del src, dst
+
+
+def _counter_means(path: str, counter: str):
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, workload: str, mib: int):
+    """Per-launch HBM bytes of each kernel from FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by bytes / counter of the calibration copy launched in the same process."""
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    calib = [k for k in fetch if CALIB_KERNEL in k]
+    if not calib:
+        raise SystemExit("no calibration copy in the counter CSV (run with --copy-calib-mib)")
+    nbytes = mib * (1 << 20)
+    cf = fetch[calib[0]]
+    cw = [v for k in write if CALIB_KERNEL in k for v in write[k]]
+    f_scale = nbytes / (np.mean(cf) * 1024.0)
+    w_scale = nbytes / (np.mean(cw) * 1024.0)
+    out_path = os.path.join(ROOT, "profiles", "traffic.json")
+    doc = json.load(open(out_path)) if os.path.exists(out_path) else {}
+    doc["_calibration"] = {"copy_bytes_each_way": nbytes, "fetch_kib": float(np.mean(cf)),
+                           "write_kib": float(np.mean(cw)), "fetch_scale": round(f_scale, 4),
+                           "write_scale": round(w_scale, 4)}
+    w = None
+    try:
+        import synth
+        w = synth.get(workload)
+    except Exception:
+        pass
+    for key, (match, src) in TRAFFIC_KERNELS.items():
+        names = [k for k in fetch if match(k)]
+        if not names:
+            continue
+        fk = np.mean([v for k in names for v in fetch[k]])
+        wk = np.mean([v for k in write if match(k) for v in write[k]])
+        if src is None:
+            src = "attn_mfma.hip" if (w is not None and w.v_from_k) else "attn_valu.hip"
+        doc[f"{key}/{workload}"] = {
+            "kernel": names[0][:120], "src_sha256_16": _src_hash(src),
+            "fetch_kib": round(float(fk), 1), "write_kib": round(float(wk), 1),
+            "bytes_per_launch": int(fk * 1024 * f_scale + wk * 1024 * w_scale),
+            "read_bytes": int(fk * 1024 * f_scale), "write_bytes": int(wk * 1024 * w_scale)}
+    json.dump(doc, open(out_path, "w"), indent=1, sort_keys=True)
+    print(json.dumps(doc, indent=1, sort_keys=True))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,7 +184,17 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="first run a plain streaming copy of this many MiB (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter CSVs of a --copy-calib-mib run into "
+                         "profiles/traffic.json and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        if not args.copy_calib_mib:
+            raise SystemExit("--summarize-counters needs the --copy-calib-mib size of the profiled run")
+        summarize_counters(*args.summarize_counters, args.workload, args.copy_calib_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decode step is sharded by request with no exchange "
               f"between GPUs, and this build runs no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -115,6 +208,8 @@ def main():
 
     tsa.load()
     w = synth.get(args.workload)
+    if args.copy_calib_mib:
+        copy_calibration(args.copy_calib_mib)
     print(f"[bench] staging {w.name}", file=sys.stderr, flush=True)
     t0 = time.time()
     st = workload.stage(w, seed=args.seed)
@@ -166,10 +261,17 @@ def main():
                      B * w.num_q_heads * w.head_dim_v * 4 + B * w.top_k * 4)
     attn_flops = float(2 * n_sel.sum() * w.num_q_heads * (w.head_dim_k + w.head_dim_v))
 
+    attn_src = "attn_mfma.hip" if w.v_from_k else "attn_valu.hip"
+
     def roof(nbytes, ms, src, key):
         gbs = nbytes / (ms * 1e-3) / 1e9
+        traffic = _traffic(src, key)
+        if key.startswith("attention/") and traffic is not None:
+            # the timed attention call is the gather kernel plus the split combine
+            comb = _traffic("attn_valu.hip", f"combine/{w.name}")
+            traffic = None if comb is None else traffic + comb
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": _traffic(src, key),
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes": nbytes, "kernel_ms": round(ms, 5)}
 
     out = {
@@ -192,7 +294,7 @@ def main():
         "kernels_ms": {"kv_append": round(t_append, 5), "indexer_score": round(t_index, 5),
                        "topk": round(t_topk, 5), "attention": round(t_attn, 5)},
         "roofline": roof(idx_bytes, t_index, "indexer_score.hip", f"indexer_score/{w.name}"),
-        "roofline_attention": dict(roof(attn_bytes, t_attn, ("attn_mfma.hip" if w.v_from_k else "attn_valu.hip"), f"attention/{w.name}"),
+        "roofline_attention": dict(roof(attn_bytes, t_attn, attn_src, f"attention/{w.name}"),
                                    flops=attn_flops,
                                    tflops=round(attn_flops / (t_attn * 1e-3) / 1e12, 2)),
         "cpu_baseline": None,

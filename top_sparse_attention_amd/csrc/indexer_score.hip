@@ -8,10 +8,15 @@
 // Opening paragraph: selecting the top k needs every cached token, so this kernel streams the
 // whole indexer cache of every request: it is bound by HBM bandwidth (1 FLOP per byte).
 //
-// Layout: a token's indexer key is index_dim bf16 values (16-byte vectors, 8 values each);
-// LPT = index_dim / 8 lanes hold one token, so one wave-wide load covers 64 / LPT whole
-// tokens (1 KiB of contiguous rows within a page), and the per-token dot product is reduced
-// across those LPT lanes.
+// A token's indexer key is index_dim bf16 values, stored contiguously, so a page of the indexer
+// cache is one contiguous run of page_size rows.  Two kernels:
+//  * single-head scores with pages of at least 16 tokens (every workload here): each wave owns
+//    a contiguous run of a request's tokens and streams it, 16 rows at a time, through a private
+//    ring of LDS slots with global-to-LDS loads (described where it is defined below);
+//  * any number of heads or smaller pages: LPT = index_dim / 8 lanes hold one token in
+//    registers (16-byte vectors, 8 values each), so one wave-wide load covers 64 / LPT whole
+//    tokens, and each head's dot product is reduced across those LPT lanes.
+// Positions whose page-table entry is not a valid page score -inf.
 #include "tsa_internal.h"
 
 namespace {

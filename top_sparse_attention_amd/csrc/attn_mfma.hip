@@ -41,7 +41,10 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;                 // selected rows per tile
-constexpr int kRing = 4;                  // tile buffers in LDS
+#ifndef TSA_RING
+#define TSA_RING 4
+#endif
+constexpr int kRing = TSA_RING;           // tile buffers in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kQkAhead = 4;               // QK k-steps whose LDS operands are read ahead
 constexpr float kHeadroom = 32.f;         // log2 headroom of the fixed softmax reference
@@ -77,6 +80,14 @@ __device__ __forceinline__ void load_lds16(const void* gsrc, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(gsrc), "s"(lds)
+                 : "memory", "m0");
+}
+
+// The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset.
+__device__ __forceinline__ void load_lds16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds)
                  : "memory", "m0");
 }
 
@@ -217,21 +228,36 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
     __syncthreads();           // rows[] and the flag visible
 
     const uint32_t ring_base = lds_addr(ring);
-    auto issue_tile = [&](int t) {
+    // Load m of this wave's share of tile t: m < 8 is region A of row wave*8 + m (one
+    // wave-wide load), m == 8 region B of rows wave*8 .. +7.  my8 holds those rows in lanes
+    // 0..7 and rowb the row of this lane's region-B chunk.
+    auto issue_part = [&](int t, int m, int32_t my8, int32_t rowb) {
         const uint32_t buf = ring_base + uint32_t((t % kRing) * G::kTileBytes);
-        const int32_t* trow = rows + t * kTile;
-        const int32_t my8 = trow[wave * 8 + (lane & 7)];      // rows wave*8 .. +7, lanes 0..7
-#pragma unroll
-        for (int m = 0; m < G::kRowsPerWaveA; ++m) {
+        if (m < G::kRowsPerWaveA) {
             const int r = wave * 8 + m;
             const int32_t row = __builtin_amdgcn_readlane(my8, m);
-            const uint16_t* src = a.kpool + int64_t(row < 0 ? 0 : row) * DK + swz_a(r, a_src_chunk) * 8;
-            load_lds16(src, __builtin_amdgcn_readfirstlane(buf + uint32_t(r * G::kRowBytesA)));
+            const uint16_t* src = a.kpool + int64_t(row < 0 ? 0 : row) * DK;   // uniform
+            load_lds16_s(src, uint32_t(swz_a(r, a_src_chunk) * 16),
+                         __builtin_amdgcn_readfirstlane(buf + uint32_t(r * G::kRowBytesA)));
+        } else {
+            const uint16_t* srcb = a.kpool + int64_t(rowb < 0 ? 0 : rowb) * DK + b_src_el;
+            load_lds16(srcb, __builtin_amdgcn_readfirstlane(buf + uint32_t(G::kBytesA + wave * 1024)));
         }
-        const int32_t rowb = trow[b_row];
-        const uint16_t* srcb = a.kpool + int64_t(rowb < 0 ? 0 : rowb) * DK + b_src_el;
-        load_lds16(srcb, __builtin_amdgcn_readfirstlane(buf + uint32_t(G::kBytesA + wave * 1024)));
     };
+    auto tile_rows = [&](int t, int32_t& my8, int32_t& rowb) {
+        my8 = rows[t * kTile + wave * 8 + (lane & 7)];
+        rowb = rows[t * kTile + b_row];
+    };
+    auto issue_tile = [&](int t) {
+        int32_t my8, rowb;
+        tile_rows(t, my8, rowb);
+#pragma unroll
+        for (int m = 0; m < kLoadsPerWave; ++m) issue_part(t, m, my8, rowb);
+    };
+    // A tile issued inside the loop is spread over the iteration: loads kQkLoads[..] after
+    // the QK k-steps listed, the rest after PV output groups, so that the load queue drains
+    // steadily instead of stalling the wave on a burst.
+    int32_t pend_t = -1, pend_my8 = 0, pend_rowb = 0;   // the tile being issued (uniform)
 
     // Softmax reference: the probabilities are exp2(logit - m_ref) with m_ref fixed at the first
     // tile where the head has a valid token, never rescaled.  Any reference gives the same
@@ -247,29 +273,41 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
     float sx[8];                 // scaled logits, then probabilities
     float stmax = -INFINITY, spsum = 0.f;
     bool sviol = false;
+    float m_use = 0.f;           // m_ref, or 0 while it is unset
     uint32_t phi_w[4], plo_w[4];
     bool scan = false;           // uniform; the workgroup is only tracking the max
     auto soft_stage = [&](int st, const f32x4 (&sc)[2], uint64_t live) {
         if (st == 0 || st == 1) {
+            if (uint32_t(live) == 0xffffffffu) {   // uniform: every token of the tile present
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 4 * st + r;
-                const int tok = st * 16 + g16 * 4 + r;
-                const float x = ((live >> tok) & 1) ? sc[st][r] * a.scale_log2 : -INFINITY;
-                sx[i] = x;
-                stmax = fmaxf(stmax, x);
+                for (int r = 0; r < 4; ++r) {
+                    const float x = sc[st][r] * a.scale_log2;
+                    sx[4 * st + r] = x;
+                    stmax = fmaxf(stmax, x);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tok = st * 16 + g16 * 4 + r;
+                    const float x = ((live >> tok) & 1) ? sc[st][r] * a.scale_log2 : -INFINITY;
+                    sx[4 * st + r] = x;
+                    stmax = fmaxf(stmax, x);
+                }
             }
         } else if (st == 2) {
             stmax = max4groups(stmax);
             m_seen = fmaxf(m_seen, stmax);
             if (m_ref == -INFINITY) m_ref = stmax;   // first tile with a valid token for the head
             sviol = stmax > m_ref + kHeadroom;
+            // exp2(-inf - m) = 0 for any finite m; before the head has a reference every
+            // logit of the tile is -inf and any finite m does
+            m_use = m_ref == -INFINITY ? 0.f : m_ref;
         } else if (st == 3) {
             if (!scan && __ballot(sviol)) *flag = 1;
         } else if (st >= 4 && st < 8) {
             const int i = 2 * (st - 4);
-            sx[i] = (sx[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sx[i] - m_ref);
-            sx[i + 1] = (sx[i + 1] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sx[i + 1] - m_ref);
+            sx[i] = __builtin_amdgcn_exp2f(sx[i] - m_use);
+            sx[i + 1] = __builtin_amdgcn_exp2f(sx[i + 1] - m_use);
             spsum += sx[i] + sx[i + 1];
         } else if (st >= 8 && st < 12) {
             // B operand of PV: P^T[kappa][head], kappa = 8*g16 + i <-> token (i < 4 ? 4*g16 + i :
@@ -312,6 +350,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
             s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks % kQkAhead][0]), qb, s[0], 0, 0, 0);
             s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks % kQkAhead][1]), qb, s[1], 0, 0, 0);
             if (with_soft && ks < kStages) soft_stage(ks, sc, live);
+            if ((ks & 3) == 1 && pend_t >= 0) issue_part(pend_t, ks >> 2, pend_my8, pend_rowb);
             __builtin_amdgcn_sched_barrier(0);
             if (ks + kQkAhead < KS) qk_read(ks + kQkAhead, kv[ks % kQkAhead]);
         }
@@ -338,6 +377,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
         for (int g = 0; g < DB / 4; ++g) {
             __builtin_amdgcn_sched_barrier(0);
             if (g + 1 < DB / 4) pv_read(4 * (g + 1), va[(g + 1) & 1]);
+            if ((g & 1) == 1 && pend_t >= 0) issue_part(pend_t, 5 + (g >> 1), pend_my8, pend_rowb);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -365,12 +405,12 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
             return __ballot(lane < kTile && t * kTile + lane < n &&
                             rows[t * kTile + (lane & (kTile - 1))] >= 0);
         };
-        if (n_tiles > 0) issue_tile(0);
-        if (n_tiles > 1) issue_tile(1);
-        if (n_tiles > 2) issue_tile(2);
+        for (int t = 0; t < kRing - 1 && t < n_tiles; ++t) issue_tile(t);
         if (n_tiles > 0) {
-            if (n_tiles > 2) wait_vm<2 * kLoadsPerWave>();
-            else if (n_tiles > 1) wait_vm<kLoadsPerWave>();
+            // tile 0 has landed once at most the later prologue tiles are outstanding
+            const int later = min(kRing - 2, n_tiles - 1);
+            if (later >= 2) wait_vm<2 * kLoadsPerWave>();
+            else if (later == 1) wait_vm<kLoadsPerWave>();
             else wait_vm<0>();
             __syncthreads();
             live_cur = live_mask(0);
@@ -379,24 +419,29 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
         for (int t = 0; t < n_tiles; ++t) {
             soft_reset();
             if (t + 1 < n_tiles) {
-                // tile t+1 has landed once at most tile t+2's loads are outstanding
-                if (t + 2 < n_tiles) wait_vm<kLoadsPerWave>();
+                // tile t+1 has landed once at most the tiles issued after it are outstanding
+                const int later = min(t + kRing - 2, n_tiles - 1) - (t + 1);
+                if (later >= 1) wait_vm<kLoadsPerWave>();
                 else wait_vm<0>();
                 __syncthreads();   // every wave's part landed; tile t-1's buffer is free again
                 scan = *flag != 0;
-                if (t + 3 < n_tiles) issue_tile(t + 3);
+                pend_t = -1;
+                if (t + kRing - 1 < n_tiles) {
+                    pend_t = t + kRing - 1;
+                    tile_rows(pend_t, pend_my8, pend_rowb);
+                }
                 live_next = live_mask(t + 1);
                 qk_tile(ring + ((t + 1) % kRing) * G::kTileBytes, s_next, true, s_cur, live_cur);
             } else {
 #pragma unroll
                 for (int st = 0; st < kStages; ++st) soft_stage(st, s_cur, live_cur);
             }
-            if (!scan) {
-                l_run += spsum;
-                pv_tile(ring + (t % kRing) * G::kTileBytes,
-                        as_bf16x8(make_uint4(phi_w[0], phi_w[1], phi_w[2], phi_w[3])),
-                        as_bf16x8(make_uint4(plo_w[0], plo_w[1], plo_w[2], plo_w[3])));
-            }
+            // In scan mode the products are discarded (the split is computed again), but PV
+            // still runs: skipping it conditionally costs the accumulators their registers.
+            l_run += spsum;
+            pv_tile(ring + (t % kRing) * G::kTileBytes,
+                    as_bf16x8(make_uint4(phi_w[0], phi_w[1], phi_w[2], phi_w[3])),
+                    as_bf16x8(make_uint4(plo_w[0], plo_w[1], plo_w[2], plo_w[3])));
             s_cur[0] = s_next[0];
             s_cur[1] = s_next[1];
             live_cur = live_next;
@@ -462,7 +507,7 @@ bool mfma_latent_applicable(const tsa_kv_pool& pool, const tsa_decode_params& p)
 int mfma_latent_chunk(const tsa_decode_params& p, int* splits) {
     const int tiles = int(ceil_div(p.top_k, kTile));
     int s = int(ceil_div(256, std::max(p.batch, 1)));   // one workgroup per CU
-    s = std::max(1, std::min(s, tiles));
+    s = std::max(1, std::min({s, tiles, 64}));   // the combine takes at most 64 splits
     const int chunk = int(ceil_div(tiles, s)) * kTile;
     *splits = int(ceil_div(p.top_k, chunk));
     return chunk;

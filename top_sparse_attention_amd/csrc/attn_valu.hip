@@ -226,24 +226,43 @@ __global__ void __launch_bounds__(kThreads) attn_valu_kernel(AttnArgs a) {
 }
 
 // Merge split partials: o = sum_s acc_s e^(m_s - M) / sum_s l_s e^(m_s - M), M = max_s m_s.
-__global__ void __launch_bounds__(kThreads) combine_kernel(const float* __restrict__ part_ml,
-                                                           const float* __restrict__ part_acc,
-                                                           int splits, int dv,
-                                                           float* __restrict__ out) {
+// One workgroup of kCombineThreads per (request, head); a lane owns 4 consecutive value dims
+// (16-byte loads, dv % 4 == 0); the split weights are computed once per workgroup.
+constexpr int kCombineThreads = 128;
+constexpr int kCombineMaxSplits = 64;
+__global__ void __launch_bounds__(kCombineThreads) combine_kernel(const float* __restrict__ part_ml,
+                                                                  const float* __restrict__ part_acc,
+                                                                  int splits, int dv,
+                                                                  float* __restrict__ out) {
+    __shared__ float wsh[kCombineMaxSplits];
     const int bh = blockIdx.x;  // b * Hq + h
     const float* ml = part_ml + int64_t(bh) * splits * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[2 * s]);
-    float L = 0.f;
-    for (int s = 0; s < splits; ++s)
-        if (ml[2 * s] != -INFINITY) L += ml[2 * s + 1] * __expf(ml[2 * s] - M);
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    for (int d = threadIdx.x; d < dv; d += kThreads) {
-        float x = 0.f;
-        for (int s = 0; s < splits; ++s)
-            if (ml[2 * s] != -INFINITY)
-                x = fmaf(part_acc[(int64_t(bh) * splits + s) * dv + d], __expf(ml[2 * s] - M), x);
-        out[int64_t(bh) * dv + d] = x * inv;
+    if (threadIdx.x < 64) {
+        // one wave: M and L by lane reduction over the splits (splits <= 64)
+        const int sl = threadIdx.x;
+        const float m = sl < splits ? ml[2 * sl] : -INFINITY;
+        float M = m;
+        for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        const float e = (m == -INFINITY) ? 0.f : __expf(m - M);
+        float L = sl < splits ? ml[2 * sl + 1] * e : 0.f;
+        for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+        if (sl < splits) wsh[sl] = L > 0.f ? e / L : 0.f;
+    }
+    __syncthreads();
+    const float4* acc = reinterpret_cast<const float4*>(part_acc + int64_t(bh) * splits * dv);
+    float4* o = reinterpret_cast<float4*>(out + int64_t(bh) * dv);
+    const int dv4 = dv >> 2;
+    for (int d = threadIdx.x; d < dv4; d += kCombineThreads) {
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int sp = 0; sp < splits; ++sp) {
+            const float w = wsh[sp];
+            const float4 v = acc[int64_t(sp) * dv4 + d];
+            x.x = fmaf(v.x, w, x.x);
+            x.y = fmaf(v.y, w, x.y);
+            x.z = fmaf(v.z, w, x.z);
+            x.w = fmaf(v.w, w, x.w);
+        }
+        o[d] = x;
     }
 }
 
@@ -308,14 +327,18 @@ bool attention_supported(const tsa_kv_pool& pool, const tsa_decode_params& p, st
     return true;
 }
 
+// Partials: (max, sum) pairs for n rows, padded to 16 bytes, then n accumulator rows of dv.
+size_t partial_ml_floats(size_t n) { return (2 * n + 3) / 4 * 4; }
+size_t partial_bytes(size_t n, int dv) { return (partial_ml_floats(n) + n * size_t(dv)) * sizeof(float); }
+
 AttnPlan plan_attention(const tsa_kv_pool& pool, const tsa_decode_params& p) {
     AttnPlan plan;
     const tsa_pool_desc& d = pool.d;
     if (mfma_latent_applicable(pool, p)) {
         plan.kind = 1;
         plan.chunk = mfma_latent_chunk(p, &plan.splits);
-        plan.partial_bytes = plan.splits > 1 ? size_t(p.batch) * p.num_q_heads * plan.splits *
-                                                   (size_t(d.head_dim_v) + 2) * sizeof(float)
+        plan.partial_bytes = plan.splits > 1 ? partial_bytes(size_t(p.batch) * p.num_q_heads * plan.splits,
+                                                             d.head_dim_v)
                                              : 0;
         return plan;
     }
@@ -324,12 +347,12 @@ AttnPlan plan_attention(const tsa_kv_pool& pool, const tsa_decode_params& p) {
     const int units = p.batch * d.num_kv_heads;
     const int tiles = int(ceil_div(p.top_k, T));
     int splits = int(ceil_div(512, units));  // aim for >= 2 workgroups per CU
-    splits = std::max(1, std::min(splits, tiles));
+    splits = std::max(1, std::min({splits, tiles, kCombineMaxSplits}));
     plan.kind = 0;
     plan.chunk = int(ceil_div(tiles, splits)) * T;
     plan.splits = int(ceil_div(p.top_k, plan.chunk));
-    plan.partial_bytes = plan.splits > 1 ? size_t(p.batch) * p.num_q_heads * plan.splits *
-                                               (size_t(d.head_dim_v) + 2) * sizeof(float)
+    plan.partial_bytes = plan.splits > 1 ? partial_bytes(size_t(p.batch) * p.num_q_heads * plan.splits,
+                                                         d.head_dim_v)
                                          : 0;
     return plan;
 }
@@ -371,7 +394,7 @@ hipError_t launch_attention(const tsa_kv_pool& pool, int layer, const tsa_decode
     a.scale = p.sm_scale;
     const size_t n_part = size_t(p.batch) * p.num_q_heads * plan.splits;
     a.part_ml = static_cast<float*>(partial);
-    a.part_acc = a.part_ml ? a.part_ml + n_part * 2 : nullptr;
+    a.part_acc = a.part_ml ? a.part_ml + partial_ml_floats(n_part) : nullptr;
 
     hipError_t e;
     if (plan.kind == 1) {
@@ -381,7 +404,7 @@ hipError_t launch_attention(const tsa_kv_pool& pool, int layer, const tsa_decode
         e = launch_valu(a, pool, p, plan, s);
     }
     if (e != hipSuccess || plan.splits == 1) return e;
-    hipLaunchKernelGGL(combine_kernel, dim3(p.batch * p.num_q_heads), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(combine_kernel, dim3(p.batch * p.num_q_heads), dim3(kCombineThreads), 0, s,
                        a.part_ml, a.part_acc, plan.splits, d.head_dim_v, out);
     return hipGetLastError();
 }

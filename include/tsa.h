@@ -218,6 +218,78 @@ tsa_status tsa_sparse_decode_attn(tsa_kv_pool* pool, int32_t layer, const tsa_de
                                   const int32_t* seq_lens_dev, float* out_dev, int32_t* topk_dev,
                                   void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * Tiered KV: an HBM page cache with LRU eviction over a host-memory copy of every page.
+ * [GLM5.3 page], HiSparse paragraph: the KV cache lives in host DRAM and the HBM part acts as
+ * an LRU cache; a top-k selection that misses loads the page from DRAM, the least recently
+ * used page is evicted, and the loads for layer N overlap the computation of layer N-1.
+ * [snapshot page], "Lợi ích thì đo được rõ": strict LRU falls off a cliff when the working
+ * set exceeds the cache (a cyclic scan hits nothing).
+ *
+ * The cache is an ordinary pool (num_layers 1, num_pages = cache slots, no indexer region);
+ * a pool created without device regions gives a bookkeeping-only tier (plan, release, stats;
+ * host_k / host_v may then be NULL and fetch is refused);
+ * a slot holds one page of any (layer, request).  Logical page keys are
+ *     key = (layer * num_req + req) * pages_per_req + page.
+ * host_k / host_v: pinned host memory (hipHostMalloc, e.g. torch pin_memory=True), key-major:
+ * page `key` occupies bytes [key * page_bytes, (key + 1) * page_bytes) with
+ * page_bytes = page_size * num_kv_heads * head_dim * 2 (the pool's K / V page).  The GPU
+ * reads missing pages from it directly (mapped pinned memory), so the host copy must stay
+ * allocated and unchanged while the cache exists.  The cache owns pinned host staging
+ * buffers for its transfer lists; it allocates no device memory.
+ *
+ * Policy (the pages leave the details open): a plan touches the distinct pages of each
+ * request's positions, requests ascending, pages ascending within a request.  A resident page
+ * is a hit and becomes most recent; a missing page takes a free slot (lowest first) or evicts
+ * the least recently touched page that no unreleased plan holds.  Pages a plan touches stay
+ * pinned until that plan's tag is released (the layer being computed and the one being
+ * fetched are both in flight).  K/V pages never change once written, so eviction writes
+ * nothing back.
+ * ---------------------------------------------------------------------------------- */
+typedef struct tsa_lru tsa_lru;
+
+/* cache: a pool with v_from_k 0, index_dim 0, num_layers 1, device K and V regions.
+ * Initially every slot is free and no page is resident. */
+tsa_status tsa_lru_create(tsa_kv_pool* cache, int32_t num_layers, int32_t num_req,
+                          int32_t pages_per_req, const void* host_k, const void* host_v,
+                          tsa_lru** out);
+tsa_status tsa_lru_destroy(tsa_lru* lru);
+
+/* Make `keys` (host int64 [n]) resident, first = least recent, without counting hits or
+ * misses; their copies join the next fetch. */
+tsa_status tsa_lru_preload(tsa_lru* lru, int64_t n, const int64_t* keys);
+
+/* Host bookkeeping for one layer.  positions: host int32 [n_req][k] token positions (entries
+ * < 0 or >= pages_per_req * page_size are ignored).  slot_table: host int32
+ * [n_req][pages_per_req], filled with the slot of every touched page and -1 elsewhere (a page
+ * table for tsa_sparse_attn_gather on the cache pool, layer 0).  The touched pages are pinned
+ * under `tag`.  n_fetch (nullable) receives the number of page copies now pending.  Fails
+ * with TSA_ERR_CAPACITY, changing nothing, if the misses exceed the free slots plus the
+ * unpinned pages the plan does not touch. */
+tsa_status tsa_lru_plan(tsa_lru* lru, int32_t layer, int64_t tag, int32_t n_req,
+                        const int32_t* positions, int32_t k, int32_t* slot_table,
+                        int64_t* n_fetch);
+
+/* Device workspace for tsa_lru_fetch with up to n_req requests per plan. */
+tsa_status tsa_lru_workspace_bytes(const tsa_lru* lru, int32_t n_req, size_t* bytes);
+
+/* Enqueue on `stream`: the slot table (host, as filled by the last plan) to slot_table_dev
+ * (int32 [n_req][pages_per_req]) and the copies of every pending page from host memory into
+ * its slot.  The caller orders `stream` after every kernel that reads a page a released tag
+ * held (eviction reuses those slots) and orders the attention of the layer after this call
+ * (e.g. with events). */
+tsa_status tsa_lru_fetch(tsa_lru* lru, int32_t n_req, const int32_t* slot_table,
+                         int32_t* slot_table_dev, void* workspace, size_t ws_bytes,
+                         void* stream);
+
+/* Unpin the pages held under `tag`. */
+tsa_status tsa_lru_release(tsa_lru* lru, int64_t tag);
+
+/* Counters since creation (preloads excluded): page touches that hit, that missed, evictions,
+ * and bytes copied from host memory (preloads included). */
+tsa_status tsa_lru_stats(const tsa_lru* lru, int64_t* hits, int64_t* misses,
+                         int64_t* evictions, int64_t* h2d_bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -91,3 +91,21 @@ class LRUCache:
 def pages_of_positions(positions, page_size: int):
     """Distinct logical pages, ascending, touched by a set of token positions."""
     return sorted({int(p) // int(page_size) for p in positions if int(p) >= 0})
+
+
+def plan_layer(cache: LRUCache, layer: int, num_req: int, pages_per_req: int, positions,
+               page_size: int, tag):
+    """One layer's plan under the tiered-cache policy: for each request in order, touch the
+    distinct pages its positions fall in, ascending, pinned under ``tag``.  The key of page
+    ``p`` of request ``r`` in ``layer`` is (layer * num_req + r) * pages_per_req + p.
+    Returns the slot table [len(positions)][pages_per_req] (-1 where untouched)."""
+    import numpy as np
+    table = np.full((len(positions), pages_per_req), -1, dtype=np.int32)
+    for r, pos in enumerate(positions):
+        for page in pages_of_positions(pos, page_size):
+            if page >= pages_per_req:
+                continue
+            key = (layer * num_req + r) * pages_per_req + page
+            slot, _ = cache.touch(key, tag)
+            table[r, page] = slot
+    return table

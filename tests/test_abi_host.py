@@ -197,3 +197,83 @@ class _FakeDev:
 
     def data_ptr(self):
         return 0
+
+
+# ---------------------------------------------------------------- tiered cache bookkeeping
+
+def _tier_positions(rng, n_req, k, length, hot):
+    """Locality-biased positions (a few hot spots plus uniform picks), distinct per request."""
+    out = np.empty((n_req, k), dtype=np.int32)
+    for r in range(n_req):
+        centres = rng.integers(0, length, size=hot)
+        loc = np.clip(centres[rng.integers(0, hot, size=2 * k)] + rng.normal(0, 200, size=2 * k), 0,
+                      length - 1).astype(np.int64)
+        pool = np.unique(np.concatenate([loc, rng.integers(0, length, size=k)]))
+        out[r] = np.sort(rng.choice(pool, size=k, replace=False))
+    return out
+
+
+@pytest.mark.parametrize("capacity,K", [(256, 96), (160, 24), (4096, 96)])
+def test_lru_tier_matches_oracle(capacity, K):
+    """Slot tables, hits, misses and evictions of the library's tier equal the oracle's under
+    the same plan / release sequence (two layers in flight), with a preloaded start."""
+    from oracle import lru
+    P, L, R, NPR = 64, 3, 4, 32
+    cache = _pool(capacity, P, kv_heads=2, dk=128, dv=128)
+    tier = tsa.LruTier(cache, L, R, NPR)
+    oc = lru.LRUCache(capacity)
+    pre = np.array([(l * R + r) * NPR + p for l in range(L) for r in range(R) for p in range(NPR - 3, NPR)
+                    if ((l * R + r) * 3 + p) % 2 == 0][:capacity // 2], dtype=np.int64)
+    tier.preload(pre)
+    oc.preload(pre.tolist())
+    rng = np.random.default_rng(capacity)
+    g = touches = 0
+    for step in range(4):
+        for layer in range(L):
+            pos = _tier_positions(rng, R, K, NPR * P, hot=3)
+            touches += sum(len(lru.pages_of_positions(p, P)) for p in pos)
+            table, _ = tier.plan(layer, g, pos)
+            ref = lru.plan_layer(oc, layer, R, NPR, pos, P, g)
+            assert np.array_equal(table, ref), (step, layer)
+            if g > 0:
+                tier.release(g - 1)
+                oc.release(g - 1)
+            g += 1
+    st = tier.stats()
+    assert (st["hits"], st["misses"], st["evictions"]) == (oc.hits, oc.misses, oc.evictions)
+    assert st["hits"] + st["misses"] == touches
+    if capacity >= L * R * NPR:
+        assert st["evictions"] == 0
+    elif K == 24:
+        assert st["hits"] > 0 and st["evictions"] > 0      # a cache that both hits and evicts
+
+
+def test_lru_tier_capacity_error_changes_nothing():
+    P, R, NPR = 64, 2, 8
+    cache = _pool(4, P, kv_heads=2, dk=128, dv=128)
+    tier = tsa.LruTier(cache, 1, R, NPR)
+    t0, _ = tier.plan(0, 0, np.array([[0, 64, 128], [-1, -1, 5]], dtype=np.int32))
+    assert sorted(t0[t0 >= 0].tolist()) == [0, 1, 2, 3]
+    before = tier.stats()
+    # tag 0 still pins all four slots: a plan that needs a new page cannot fit
+    with pytest.raises(tsa.TsaError) as e:
+        tier.plan(0, 1, np.array([[0, 200, 300], [5, 6, 7]], dtype=np.int32))
+    assert e.value.status == _lib.TSA_ERR_CAPACITY
+    assert tier.stats() == before
+    # hits only: fits even with everything pinned
+    t1, _ = tier.plan(0, 1, np.array([[0, 65, 130], [1, 2, 3]], dtype=np.int32))
+    assert np.array_equal(t1, t0)
+    tier.release(0)
+    tier.release(1)
+    with pytest.raises(tsa.TsaError):
+        tier.release(1)
+    t2, _ = tier.plan(0, 2, np.array([[300, 301, 302], [-1, -1, -1]], dtype=np.int32))
+    assert t2[0, 4] >= 0 and tier.stats()["evictions"] == 1
+
+
+def test_lru_tier_refuses_fetch_without_device_memory():
+    cache = _pool(8, 64, kv_heads=2, dk=128, dv=128)
+    tier = tsa.LruTier(cache, 1, 1, 4)
+    table, _ = tier.plan(0, 0, np.array([[0]], dtype=np.int32))
+    with pytest.raises(tsa.TsaError):
+        _lib.call("tsa_lru_fetch", tier.handle, 1, table.ctypes.data_as(_lib.P_i32), None, None, 0, None)

@@ -151,6 +151,76 @@ class KvPool:
              _ptr(idx_src), _ptr(bad_dev), _stream(stream))
 
 
+class LruTier:
+    """HBM page cache with LRU eviction over a pinned host copy of every page (tsa_lru_*).
+
+    ``cache`` is a one-layer KvPool holding the slots (no indexer, separate V); ``host_k`` /
+    ``host_v`` are pinned host tensors, key-major pages (key = (layer * num_req + req) *
+    pages_per_req + page).  With a metadata-only cache (allocate=False) the tier only does
+    the bookkeeping."""
+
+    def __init__(self, cache: KvPool, num_layers: int, num_req: int, pages_per_req: int,
+                 host_k=None, host_v=None):
+        self.cache = cache
+        self.num_req = int(num_req)
+        self.pages_per_req = int(pages_per_req)
+        self._host = (host_k, host_v)       # kept alive: the GPU reads them
+        h = _lib.vp()
+        call("tsa_lru_create", cache.handle, int(num_layers), int(num_req), int(pages_per_req),
+             _ptr(host_k), _ptr(host_v), C.byref(h))
+        self.handle = h
+        self.workspace = None
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            _lib.load().tsa_lru_destroy(self.handle)
+            self.handle = _lib.vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def preload(self, keys):
+        keys = np.ascontiguousarray(keys, dtype=np.int64)
+        call("tsa_lru_preload", self.handle, int(keys.shape[0]), keys.ctypes.data_as(_lib.P_i64))
+
+    def plan(self, layer: int, tag: int, positions: np.ndarray):
+        """positions: int32 [n_req, k].  Returns (slot_table int32 [n_req, pages_per_req],
+        pending copies)."""
+        positions = np.ascontiguousarray(positions, dtype=np.int32)
+        n_req, k = positions.shape
+        table = np.empty((n_req, self.pages_per_req), dtype=np.int32)
+        nf = _lib.i64()
+        call("tsa_lru_plan", self.handle, int(layer), int(tag), int(n_req), _i32p(positions), int(k),
+             _i32p(table), C.byref(nf))
+        return table, nf.value
+
+    def workspace_bytes(self, n_req: int) -> int:
+        b = _lib.sz()
+        call("tsa_lru_workspace_bytes", self.handle, int(n_req), C.byref(b))
+        return b.value
+
+    def fetch(self, table: np.ndarray, table_dev, stream=None):
+        """Upload the slot table and copy the pending pages (enqueued on ``stream``)."""
+        import torch
+        table = np.ascontiguousarray(table, dtype=np.int32)
+        if self.workspace is None:
+            self.workspace = torch.empty(max(self.workspace_bytes(table.shape[0]), 256), dtype=torch.uint8,
+                                         device=self.cache.k.device)
+        call("tsa_lru_fetch", self.handle, int(table.shape[0]), _i32p(table), _ptr(table_dev),
+             _ptr(self.workspace), _nbytes(self.workspace), _stream(stream))
+
+    def release(self, tag: int):
+        call("tsa_lru_release", self.handle, int(tag))
+
+    def stats(self):
+        v = [_lib.i64() for _ in range(4)]
+        call("tsa_lru_stats", self.handle, *[C.byref(x) for x in v])
+        return {"hits": v[0].value, "misses": v[1].value, "evictions": v[2].value, "h2d_bytes": v[3].value}
+
+
 def workspace_bytes(pool: KvPool, p: DecodeParams) -> int:
     n = _lib.sz()
     call("tsa_sparse_decode_workspace", pool.handle, C.byref(p), C.byref(n))

@@ -54,6 +54,14 @@ SIGNATURES = {
     "tsa_sparse_attn_gather": (i32, [vp, i32, C.POINTER(DecodeParams), vp, vp, vp, i32, vp, vp, vp, sz, vp]),
     "tsa_sparse_decode_attn": (i32, [vp, i32, C.POINTER(DecodeParams), vp, vp, vp, vp, i32, vp, vp, vp,
                                      vp, sz, vp]),
+    "tsa_lru_create": (i32, [vp, i32, i32, i32, vp, vp, C.POINTER(vp)]),
+    "tsa_lru_destroy": (i32, [vp]),
+    "tsa_lru_preload": (i32, [vp, i64, P_i64]),
+    "tsa_lru_plan": (i32, [vp, i32, i64, i32, P_i32, i32, P_i32, P_i64]),
+    "tsa_lru_workspace_bytes": (i32, [vp, i32, P_sz]),
+    "tsa_lru_fetch": (i32, [vp, i32, P_i32, vp, vp, sz, vp]),
+    "tsa_lru_release": (i32, [vp, i64]),
+    "tsa_lru_stats": (i32, [vp, P_i64, P_i64, P_i64, P_i64]),
 }
 
 _lib = None

@@ -142,3 +142,79 @@ def stage(w, seed: int = 0, batch: Optional[int] = None, lens: Optional[np.ndarr
     st.qidx_np = qidx_np
     st.q_np = q_np
     return st
+
+
+@dataclasses.dataclass
+class StagedTier:
+    """A tiered workload: every page in pinned host memory, an HBM cache of ``cache_pages``
+    slots managed by an LruTier, and the per-layer attention call over the cache."""
+    w: object
+    seed: int
+    num_req: int
+    length: int
+    pages_per_req: int
+    host_k: object
+    host_v: object
+    cache: KvPool
+    tier: object
+    params: object
+    q: object
+    lens_dev: object
+    workspace: object
+
+    def key(self, layer: int, req: int, page: int) -> int:
+        return (layer * self.num_req + req) * self.pages_per_req + page
+
+    def positions(self, step: int, layer: int, centres: dict):
+        """Seeded per-(step, layer) positions for every request, int32 [num_req, top_k]."""
+        import synth
+        out = np.empty((self.num_req, self.w.top_k), dtype=np.int32)
+        for r in range(self.num_req):
+            out[r], centres[(layer, r)] = synth.tier_positions(self.w, self.seed, step, layer, r,
+                                                               centres.get((layer, r)))
+        return out
+
+    def attend(self, table_dev, topk_dev, out, stream=None):
+        """Attention of one layer over the cache, through its slot table."""
+        from . import sparse_attn_gather
+        sparse_attn_gather(self.cache, 0, self.params, self.q, topk_dev, table_dev, self.lens_dev,
+                           out, self.workspace, stream=stream)
+
+
+def stage_tier(w, seed: int = 0, num_req: Optional[int] = None, length: Optional[int] = None,
+               num_layers: Optional[int] = None, top_k: Optional[int] = None,
+               cache_pages: Optional[int] = None, device: str = "cuda") -> StagedTier:
+    """Stage the tiered workload ``w`` (optionally scaled down): fill the pinned host copy of
+    every (layer, request) page from ``synth`` and create an empty HBM cache.  The default
+    cache holds ``w.cache_fraction`` of all pages."""
+    import torch
+    import synth
+    from . import LruTier
+
+    R = w.batch if num_req is None else int(num_req)
+    L = int(w.fixed_lens[0]) if length is None else int(length)
+    NL = w.num_layers if num_layers is None else int(num_layers)
+    k = w.top_k if top_k is None else int(top_k)
+    w = dataclasses.replace(w, batch=R, fixed_lens=(L,) * R, num_layers=NL, top_k=k)
+    P = w.page_size
+    npr = -(-L // P)
+    keys = NL * R * npr
+    C = int(round(keys * w.cache_fraction)) if cache_pages is None else int(cache_pages)
+    row = w.num_kv_heads * w.head_dim_k
+    host_k = torch.empty((keys * P, row), dtype=torch.bfloat16, pin_memory=True)
+    host_v = torch.empty((keys * P, row), dtype=torch.bfloat16, pin_memory=True)
+    hk = host_k.view(torch.int16).numpy()
+    hv = host_v.view(torch.int16).numpy()
+    for layer in range(NL):
+        for r in range(R):
+            _, kk, vv = synth.request_tokens(w, seed, r, L, layer=layer)
+            base = ((layer * R + r) * npr) * P
+            hk[base:base + L] = kk.reshape(L, row).view(np.int16)
+            hv[base:base + L] = vv.reshape(L, row).view(np.int16)
+    cache = KvPool(C, P, w.num_kv_heads, w.head_dim_k, w.head_dim_v, device=device)
+    tier = LruTier(cache, NL, R, npr, host_k, host_v)
+    q = _dev(synth.queries(w, seed), device)
+    params = decode_params(R, w.num_q_heads, k, L, w.sm_scale)
+    ws = torch.empty(max(workspace_bytes(cache, params), 256), dtype=torch.uint8, device=device)
+    lens_dev = torch.full((R,), L, dtype=torch.int32, device=device)
+    return StagedTier(w, seed, R, L, npr, host_k, host_v, cache, tier, params, q, lens_dev, ws)

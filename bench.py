@@ -16,6 +16,7 @@ HIP events recorded on the launch stream around each launch inside the timed reg
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -175,6 +176,127 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, mib: int):
     print(json.dumps(doc, indent=1, sort_keys=True))
 
 
+def bench_tier(args):
+    """The tiered workload: per step, every layer plans its pages on the host, fetches the
+    misses on a side stream and attends over the HBM cache; prints one JSON line with
+    tokens/s (requests decoded per second), the hit rate and the host-to-device rate.  The
+    host copy of every page holds seeded random bf16 values (a repeated block: the tier's
+    timing does not depend on them); positions come from the seeded locality-biased
+    generator and are drawn before timing."""
+    import torch
+    import synth
+    import top_sparse_attention_amd as tsa
+    from top_sparse_attention_amd import KvPool, LruTier, decode_params, workspace_bytes
+
+    tsa.load()
+    w = synth.get(args.workload)
+    R = args.tier_requests
+    L = int(w.fixed_lens[0])
+    NL, P, k = w.num_layers, w.page_size, w.top_k
+    w = dataclasses.replace(w, batch=R, fixed_lens=(L,) * R)
+    npr = -(-L // P)
+    keys = NL * R * npr
+    C = int(round(keys * w.cache_fraction))
+    row = w.num_kv_heads * w.head_dim_k
+    print(f"[bench] tier: {R} requests x {L} tokens x {NL} layers, {keys} pages "
+          f"({2 * keys * P * row * 2 / 2**30:.1f} GiB pinned), cache {C} slots", file=sys.stderr, flush=True)
+    g = torch.Generator().manual_seed(args.seed)
+    host_k = torch.empty((keys * P, row), dtype=torch.bfloat16, pin_memory=True)
+    host_v = torch.empty((keys * P, row), dtype=torch.bfloat16, pin_memory=True)
+    # a 64 MiB seeded random block repeated over the whole host copy (drawing every value
+    # would take minutes; the tier's timing does not depend on them)
+    block = torch.empty(1 << 25, dtype=torch.bfloat16)
+    for i in range(0, block.numel(), 1 << 22):
+        block[i:i + (1 << 22)].normal_(0.0, w.kv_std, generator=g)
+    for t in (host_k, host_v):
+        flat = t.view(-1)
+        for i in range(0, flat.numel(), block.numel()):
+            n = min(block.numel(), flat.numel() - i)
+            flat[i:i + n].copy_(block[:n])
+    cache = KvPool(C, P, w.num_kv_heads, w.head_dim_k, w.head_dim_v)
+    tier = LruTier(cache, NL, R, npr, host_k, host_v)
+    # initial state: the last quarter of every (layer, request)'s pages, in key order
+    keep = max(1, npr // 4)
+    pre = np.array([(l * R + r) * npr + p for l in range(NL) for r in range(R) for p in range(npr - keep, npr)],
+                   dtype=np.int64)[:C]
+    tier.preload(pre)
+    params = decode_params(R, w.num_q_heads, k, L, w.sm_scale)
+    ws = torch.empty(max(workspace_bytes(cache, params), 256), dtype=torch.uint8, device="cuda")
+    lens_dev = torch.full((R,), L, dtype=torch.int32, device="cuda")
+    q = torch.from_numpy(synth.queries(w, args.seed).view(np.int16)).cuda()
+    out = torch.empty((R, w.num_q_heads, w.head_dim_v), dtype=torch.float32, device="cuda")
+    total_steps = args.warmup + args.steps
+    centres, pos_all = {}, []
+    for step in range(total_steps):
+        layer_pos = []
+        for layer in range(NL):
+            a = np.empty((R, k), dtype=np.int32)
+            for r in range(R):
+                a[r], centres[(layer, r)] = synth.tier_positions(w, args.seed, step, layer, r,
+                                                                 centres.get((layer, r)))
+            layer_pos.append(a)
+        pos_all.append(layer_pos)
+    pos_dev = [[torch.from_numpy(a).cuda() for a in lp] for lp in pos_all]
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    table_dev = [torch.empty((R, npr), dtype=torch.int32, device="cuda") for _ in range(2)]
+    fetched = [torch.cuda.Event() for _ in range(2)]
+    done = {}
+    ev_attn = []
+    gidx = 0
+
+    def run_step(step, timed):
+        nonlocal gidx
+        for layer in range(NL):
+            table, _ = tier.plan(layer, gidx, pos_all[step][layer])
+            if gidx - 2 in done:
+                side.wait_event(done[gidx - 2])
+            tier.fetch(table, table_dev[gidx & 1], stream=side)
+            fetched[gidx & 1].record(side)
+            main.wait_event(fetched[gidx & 1])
+            e0 = torch.cuda.Event(enable_timing=True) if timed else None
+            if timed:
+                e0.record(main)
+            tsa.sparse_attn_gather(cache, 0, params, q, pos_dev[step][layer], table_dev[gidx & 1], lens_dev,
+                                   out, ws)
+            ev = torch.cuda.Event(enable_timing=timed)
+            ev.record(main)
+            done[gidx] = ev
+            if timed:
+                ev_attn.append((e0, ev))
+            if gidx > 0:
+                tier.release(gidx - 1)
+            gidx += 1
+
+    for s_ in range(args.warmup):
+        run_step(s_, False)
+    torch.cuda.synchronize()
+    st0 = tier.stats()
+    t0 = time.perf_counter()
+    for s_ in range(args.warmup, total_steps):
+        run_step(s_, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    st1 = tier.stats()
+    hits, misses = st1["hits"] - st0["hits"], st1["misses"] - st0["misses"]
+    h2d = st1["h2d_bytes"] - st0["h2d_bytes"]
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_attn]))
+    ms_step = elapsed * 1e3 / args.steps
+    res = {
+        "metric": "tiered sparse decode tokens/s (8 layers per token) and HBM page-cache hit rate",
+        "value": round(R / (ms_step * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "requests": R, "context": L, "layers": NL, "top_k": k,
+                   "page_size": P, "cache_pages": C, "logical_pages": keys, "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim_k, "parallelism": "none"},
+        "tier": {"hit_rate": round(hits / max(hits + misses, 1), 4), "hits": hits, "misses": misses,
+                 "h2d_GBps": round(h2d / elapsed / 1e9, 2), "h2d_bytes_per_step": h2d // args.steps,
+                 "attention_ms_per_layer": round(attn_ms, 4)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +306,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--tier-requests", type=int, default=16,
+                    help="requests of the tiered workload (the full 256 needs 128 GiB of pinned memory)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run a plain streaming copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -206,6 +330,9 @@ def main():
     import top_sparse_attention_amd as tsa
     from top_sparse_attention_amd import workload
 
+    if synth.get(args.workload).num_layers > 1:
+        bench_tier(args)
+        return
     tsa.load()
     w = synth.get(args.workload)
     if args.copy_calib_mib:

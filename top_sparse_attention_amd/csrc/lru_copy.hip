@@ -3,8 +3,8 @@
 // GLM5.3 sparse-attention page, HiSparse paragraph: a top-k selection that misses the HBM
 // cache loads the page from host DRAM.  Rather than one DMA call per 32 KiB page (whose
 // per-call cost would dominate thousands of misses per layer), one kernel reads the mapped
-// host memory directly over the host link: a workgroup per missed page, each lane moving
-// 16-byte vectors, K page then V page, with several loads in flight per lane.
+// host memory directly over the host link: a few workgroups walk the list of missed pages,
+// each lane moving 16-byte vectors, K page then V page, with several loads in flight.
 #include "tsa_internal.h"
 
 struct tsa_lru;
@@ -19,7 +19,10 @@ const tsa_kv_pool& lru_cache(const tsa_lru& l);
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;
+// Workgroups of the copy: enough 16-byte loads in flight to fill the host link (64 x 256
+// lanes x 8 loads = 2 MiB), few enough that the attention running beside it keeps the CUs.
+constexpr int kCopyGroups = 64;
 
 __global__ void __launch_bounds__(kThreads) lru_copy_kernel(const int64_t* __restrict__ keys,
                                                             const int32_t* __restrict__ slots,
@@ -62,7 +65,7 @@ hipError_t launch_lru_copy(const tsa_lru& lru, const int64_t* keys_dev, const in
     const tsa_kv_pool& cache = lru_cache(lru);
     const size_t pb = lru_page_bytes(lru);
     if (pb % 16 != 0) return hipErrorInvalidValue;
-    const int64_t grid = std::min<int64_t>(n, 65536);
+    const int64_t grid = std::min<int64_t>(n, kCopyGroups);
     hipLaunchKernelGGL(lru_copy_kernel, dim3(unsigned(grid)), dim3(kThreads), 0, s, keys_dev, slots_dev, n,
                        int64_t(pb / 16), reinterpret_cast<const uint4*>(lru_host_k(lru)),
                        reinterpret_cast<const uint4*>(lru_host_v(lru)), static_cast<uint4*>(cache.k),

@@ -10,10 +10,10 @@
 // also finds the smallest and largest candidate key; when they are equal the threshold key is
 // known and the remaining passes are skipped (ties at the threshold are common for
 // integer-valued scores).  After the passes, every element whose key exceeds the threshold is
-// kept, and of the elements equal
-// to it the lowest positions fill the rest; a block-wide scan over positions (each thread
-// owns a contiguous run of positions) yields both the tie ranks and the output offsets, so the
-// output comes out ascending with no sort.
+// kept, and of the elements equal to it the lowest positions fill the rest; one block-wide
+// scan over positions (each thread owns a contiguous run) of the packed counts (above,
+// equal) yields both the tie ranks and the output offsets, so the output comes out ascending
+// with no sort.
 #include "tsa_internal.h"
 
 namespace {
@@ -29,28 +29,29 @@ __device__ inline uint32_t order_key(float f) {
 
 // Exclusive scan over the block in thread order; returns this thread's prefix, total in *total.
 __device__ inline int block_exclusive_scan(int v, int* sh_waves, int* total) {
+    // sums wrap modulo 2^32 (unsigned arithmetic): packed counts rely on it
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
+    uint32_t x = uint32_t(v);
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o);
+        const uint32_t y = uint32_t(__shfl_up(int(x), o));
         if (lane >= o) x += y;
     }
-    if (lane == 63) sh_waves[wave] = x;
+    if (lane == 63) sh_waves[wave] = int(x);
     __syncthreads();
     if (threadIdx.x < 64) {
-        int w = threadIdx.x < kWaves ? sh_waves[threadIdx.x] : 0;
-        int s = w;
+        const uint32_t w = threadIdx.x < kWaves ? uint32_t(sh_waves[threadIdx.x]) : 0u;
+        uint32_t s = w;
 #pragma unroll
         for (int o = 1; o < kWaves; o <<= 1) {
-            int y = __shfl_up(s, o);
+            const uint32_t y = uint32_t(__shfl_up(int(s), o));
             if ((int)threadIdx.x >= o) s += y;
         }
-        if (threadIdx.x < kWaves) sh_waves[kWaves + threadIdx.x] = s - w;
-        if (threadIdx.x == kWaves - 1) sh_waves[2 * kWaves] = s;
+        if (threadIdx.x < kWaves) sh_waves[kWaves + threadIdx.x] = int(s - w);
+        if (threadIdx.x == kWaves - 1) sh_waves[2 * kWaves] = int(s);
     }
     __syncthreads();
-    int r = sh_waves[kWaves + wave] + x - v;
+    const int r = int(uint32_t(sh_waves[kWaves + wave]) + x - uint32_t(v));
     *total = sh_waves[2 * kWaves];
     __syncthreads();
     return r;
@@ -160,34 +161,31 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
         if (in_bin == remaining) break;  // the whole bin is kept: no finer digit matters
     }
 
-    // final selection: above the threshold, or equal to it and among the first `remaining`
-    int eq = 0;
-#pragma unroll
-    for (int i = 0; i < IPT; ++i) eq += (base + i < len && (key[i] & mask) == prefix);
-    int dummy;
-    int eq_before = block_exclusive_scan(eq, sh_scan, &dummy);
-    int nsel = 0;
-    uint64_t selbits = 0;
+    // final selection: above the threshold, or equal to it and among the first `remaining`;
+    // one scan of the packed counts (above << 16 | equal): an exclusive prefix of either count
+    // stays below 2^16 (at most 64 * kThreads elements, fewer than k above the threshold), so
+    // the low field never carries into the high one
+    int gt = 0, eq = 0;
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-        bool v = base + i < len;
-        uint32_t m = key[i] & mask;
-        bool take = false;
-        if (v && m > prefix) take = true;
-        if (v && m == prefix) {
-            take = eq_before < remaining;
-            ++eq_before;
-        }
-        if (take) {
-            selbits |= uint64_t(1) << i;
-            ++nsel;
-        }
+        const bool v = base + i < len;
+        const uint32_t m = key[i] & mask;
+        gt += (v && m > prefix);
+        eq += (v && m == prefix);
     }
     int total;
-    int off = block_exclusive_scan(nsel, sh_scan, &total);
+    const uint32_t packed = uint32_t(block_exclusive_scan(int((uint32_t(gt) << 16) | uint32_t(eq)), sh_scan, &total));
+    const int gt_before = int(packed >> 16), eq_before = int(packed & 0xffffu);
+    // output offset: every earlier element above, plus the earlier equal ones that are kept
+    int off = gt_before + min(eq_before, remaining);
+    int eq_rank = eq_before;
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-        if (((selbits >> i) & 1) && off < k) o[off++] = base + i;
+        const bool v = base + i < len;
+        const uint32_t m = key[i] & mask;
+        bool take = v && m > prefix;
+        if (v && m == prefix) take = eq_rank++ < remaining;
+        if (take && off < k) o[off++] = base + i;
     }
 }
 

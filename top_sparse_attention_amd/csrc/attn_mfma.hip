@@ -77,7 +77,7 @@ __device__ __forceinline__ uint32_t lds_addr(const unsigned char* p) {
 
 // Wave-wide global-to-LDS load: lane i's 16 bytes land at (uniform) lds + 16 * i.
 __device__ __forceinline__ void load_lds16(const void* gsrc, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" TSA_LOAD_POLICY
                  :
                  : "v"(gsrc), "s"(lds)
                  : "memory", "m0");
@@ -85,7 +85,7 @@ __device__ __forceinline__ void load_lds16(const void* gsrc, uint32_t lds) {
 
 // The same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte offset.
 __device__ __forceinline__ void load_lds16_s(const void* sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" TSA_LOAD_POLICY
                  :
                  : "v"(voff), "s"(sbase), "s"(lds)
                  : "memory", "m0");

@@ -129,7 +129,7 @@ constexpr int kMinPage = 16;          // smallest page size this kernel takes
 constexpr int kPagesPerWave = kMaxTpw / kMinPage + 2;
 
 __device__ __forceinline__ void load_lds16(const void* gsrc, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" TSA_LOAD_POLICY
                  :
                  : "v"(gsrc), "s"(lds)
                  : "memory", "m0");

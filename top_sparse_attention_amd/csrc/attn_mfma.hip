@@ -6,28 +6,37 @@
 // QK^T and PV are dense contractions (roofline paragraph: about 120 FLOP per byte at the GLM-5
 // shape, far above what the vector ALUs sustain per byte of HBM bandwidth).
 //
-// Formulation per workgroup (one request, one split of its selected tokens; four waves, each
-// owning 16 query heads):
+// Formulation per workgroup (one request, one split of its selected tokens), for each group of
+// 16 query heads:
 //   S^T [tokens x heads] = K_tile [tokens x dk] . Q^T [dk x heads]      (MFMA 16x16x32 bf16)
 //       A operand: K rows read from LDS (token-major, 16 bytes per lane)
-//       B operand: the wave's queries, held in registers for the whole kernel
-//   online softmax over the token axis, per head (a lane always holds one head's column)
+//       B operand: the group's queries, held in registers for the whole kernel
+//   softmax over the token axis, per head (a lane always holds one head's column)
 //   O^T [dv x heads] += V^T [dv x tokens] . P^T [tokens x heads]        (MFMA 16x16x32 bf16)
 //       A operand: the same LDS tile read with the LDS transpose load, which hands each lane
 //                  4 consecutive tokens of one value dim, so no transposed copy is stored
-//       B operand: P taken straight from the S^T accumulators (the contraction runs over the
+//       B operand: P in the layout of the S^T accumulators (the contraction runs over the
 //                  tokens in a permuted order; A and B use the same permutation)
 // P is split into bf16 hi + lo parts (two PV MFMAs) so the probabilities keep ~16 bits.
 //
+// Warp specialisation: each head group has two waves on the same SIMD.  The QK wave holds the
+// queries and computes S and the softmax of tile t+1; the PV wave holds the O^T accumulators
+// and multiplies tile t by P(t), which it reads from LDS.  Queries (72 registers) and
+// accumulators (128) then live in different waves, so two waves fit per SIMD and one wave's
+// matrix work overlaps the other's LDS reads, softmax and load issue.  (With one wave per SIMD
+// doing both, those phases ran back to back.)
+//
 // Data movement: tiles of 32 selected rows are gathered from the page table straight into LDS
-// with global-to-LDS loads (no staging registers), into a ring of 4 buffers so that 3 tiles
-// stream in while one is computed.  The loads are issued from inline assembly and waited for
+// with global-to-LDS loads (no staging registers), into a ring of 4 buffers so that two tiles
+// stream in while two are computed.  The loads are issued from inline assembly and waited for
 // with explicit vector-memory counts: the compiler would otherwise wait for every outstanding
 // LDS-bound load before the first LDS read, which serialises the ring.  A tile is stored as two
 // regions: the first DV dims of each row (value dims, DV/8 16-byte chunks, one wave-wide load
 // per row) and the remaining DK-DV dims (8 chunks per row, one load per 8 rows).  Within each
 // region the chunk index is XOR-swizzled with the row so that row-parallel operand reads spread
-// over the LDS banks.
+// over the LDS banks.  An LDS-bound load blocks its wave at issue for a long time, so each
+// wave's share of a tile is spread over its matrix work: the QK waves load 6 value rows each,
+// the PV waves 2 value rows and 8 rows of the rope dims.
 #include "tsa_internal.h"
 
 namespace {
@@ -38,16 +47,21 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-constexpr int kWaves = 4;
+constexpr int kGroups = 4;                // head groups of 16 query heads
+constexpr int kWaves = 2 * kGroups;       // per group: a QK + softmax wave and a PV wave
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;                 // selected rows per tile
-#ifndef TSA_RING
-#define TSA_RING 4
-#endif
-constexpr int kRing = TSA_RING;           // tile buffers in LDS
+constexpr int kRing = 4;                  // tile buffers in LDS
+constexpr int kRowsQ = 6;                 // value-region rows each QK wave loads per tile
+constexpr int kRowsP = (kTile - kGroups * kRowsQ) / kGroups;   // ... each PV wave (2)
+constexpr int kLoadsQK = kRowsQ;          // loads per tile of a QK wave
+constexpr int kLoadsPV = kRowsP + 1;      // ... of a PV wave: its rows + 8 rows of region B
+constexpr int kPBytes = 64 * 32;          // P of one group: 64 lanes x (hi 16 B, lo 16 B)
+constexpr int kMaxChunk = 1024;           // selected tokens per workgroup (LDS row list)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kQkAhead = 4;               // QK k-steps whose LDS operands are read ahead
 constexpr float kHeadroom = 32.f;         // log2 headroom of the fixed softmax reference
+static_assert(kGroups * (kRowsQ + kRowsP) == kTile, "every value row loaded once");
 
 template <int DK, int DV>
 struct Geo {
@@ -57,12 +71,10 @@ struct Geo {
     static constexpr int kRowBytesB = (DK - DV) * 2;
     static constexpr int kBytesA = kTile * kRowBytesA;
     static constexpr int kTileBytes = kTile * (kRowBytesA + kRowBytesB);
-    static constexpr int kRowsPerWaveA = kTile / kWaves;    // one load per row of region A
     static_assert(kChunksA == 64, "region A rows are one wave-wide load each");
     static_assert(kChunksB == 8, "region B holds 8 chunks of 8 rows per load");
-    static_assert(kTile / 8 == kWaves, "one region-B load per wave");
+    static_assert(kTile / 8 == kGroups, "one region-B load per PV wave");
 };
-constexpr int kLoadsPerWave = kTile / kWaves + 1;
 
 // stored chunk position of logical chunk c of tile row r, region A (groups of 16 chunks) and
 // region B (8 chunks per row); both are involutions on c
@@ -147,16 +159,22 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
     using G = Geo<DK, DV>;
     constexpr int KS = DK / 32;   // QK k-steps (the first KSA read region A, the rest region B)
     constexpr int KSA = DV / 32;
-    constexpr int DB = DV / 16;   // output dim blocks per wave
+    constexpr int DB = DV / 16;   // output dim blocks of a PV wave
     extern __shared__ __align__(16) unsigned char smem[];
-    unsigned char* ring = smem;                                                // kRing tiles
-    int32_t* flag = reinterpret_cast<int32_t*>(smem + kRing * G::kTileBytes);  // rescan request
-    int32_t* rows = flag + 4;                                                   // [chunk]
+    unsigned char* ring = smem;                                     // kRing tiles
+    unsigned char* pbuf = smem + kRing * G::kTileBytes;             // [group][hi 1 KiB, lo 1 KiB]
+    float* lbuf = reinterpret_cast<float*>(pbuf + kGroups * kPBytes);   // [head][m, l]
+    int32_t* flag = reinterpret_cast<int32_t*>(lbuf + 2 * kGroups * 16);  // rescan request
+    int32_t* pv_seen = flag + 4;                                    // [group] P reads done
+    int32_t* rows = pv_seen + kGroups;                              // [chunk]
 
     const int s_idx = blockIdx.x, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool is_qk = wave < kGroups;          // uniform
+    const int grp = wave & (kGroups - 1);
     const int g16 = lane >> 4, j16 = lane & 15;
-    const int h0 = blockIdx.y * (kWaves * 16) + wave * 16;   // this wave's first head
+    const int h0 = blockIdx.y * (kGroups * 16) + grp * 16;   // the group's first head
 
     int len = a.seq_lens[b];
     len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
@@ -166,8 +184,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
     const int n = max(j1 - j0, 0);
     const int n_tiles = (n + kTile - 1) / kTile;
 
-    // resolve this split's selected positions to physical rows (-1 = absent: such rows are
-    // fetched from slot 0 like any other row and masked out of the softmax)
+    // physical rows of this split's selected positions (-1 = absent: fetched from slot 0 like
+    // any other row and masked out of the softmax)
     {
         const int32_t* sel = a.topk + int64_t(b) * a.k;
         const int32_t* pt = a.page_table + int64_t(b) * a.max_pages;
@@ -184,19 +202,10 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
         }
     }
 
-    // queries of this wave's 16 heads, as the B operand of S^T = K Q^T
-    uint4 qreg[KS];
-    {
-        const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.hq + h0 + j16) * DK);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qreg[ks] = qsrc[ks * 4 + g16];
-    }
-
-    f32x4 acc[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_ref = -INFINITY;   // reference max (log2 units) of head h0 + j16
-    float l_run = 0.f;         // this lane's share of the running sum
+    uint4 qreg[KS];            // QK waves: the group's queries, B operand of S^T = K Q^T
+    float m_ref = -INFINITY;   // QK waves: reference max (log2 units) of head h0 + j16
+    float m_seen = -INFINITY;  // QK waves: max logit seen
+    float l_run = 0.f;         // QK waves: this lane's share of the running sum
 
     // lane-constant byte offsets inside a tile:
     //  QK, region A: row j16 (+16 for the second block), chunk ks*4 + g16 = 16*(ks/4) +
@@ -217,121 +226,65 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
         for (int u = 0; u < 8; ++u)
             pv_off[u] = r0 * G::kRowBytesA + swz_a(r0, 2 * u + (e0 >> 3)) * 16 + (e0 & 7) * 2;
     }
-    // loads: region A row r = wave*8 + m is one wave-wide load (lane = stored chunk position);
-    // region B rows wave*8 .. wave*8+7 are one load (lane = 8 * row-in-group + stored chunk)
-    const int a_src_chunk = lane;                      // XORed with the row's swizzle per load
-    const int b_row = wave * 8 + (lane >> 3);
+    // loads: QK wave q fetches region A of rows q*kRowsQ .. (one wave-wide load per row, lane
+    // = stored chunk position); PV wave p region A of rows kGroups*kRowsQ + p*kRowsP .. and
+    // region B of rows 8p .. 8p+7 (lane = 8 * row-in-group + stored chunk position)
+    const int a_src_chunk = lane;
+    const int my_rows = is_qk ? kRowsQ : kRowsP;
+    const int row_base = is_qk ? grp * kRowsQ : kGroups * kRowsQ + grp * kRowsP;
+    const int my_loads = is_qk ? kLoadsQK : kLoadsPV;
+    const int b_row = (grp * 8 + (lane >> 3)) & (kTile - 1);
     const int b_src_el = DV + swz_b(b_row, lane & 7) * 8;
 
-    wait_vm<0>();              // query registers loaded
     if (tid == 0) *flag = 0;
-    __syncthreads();           // rows[] and the flag visible
+    if (tid < kGroups) pv_seen[tid] = 0;
+    __syncthreads();           // rows[], the flag and the counts visible
 
     const uint32_t ring_base = lds_addr(ring);
-    // Load m of this wave's share of tile t: m < 8 is region A of row wave*8 + m (one
-    // wave-wide load), m == 8 region B of rows wave*8 .. +7.  my8 holds those rows in lanes
-    // 0..7 and rowb the row of this lane's region-B chunk.
-    auto issue_part = [&](int t, int m, int32_t my8, int32_t rowb) {
+    // Load m of this wave's share of tile t: m < my_rows is region A of row row_base + m, the
+    // next (PV waves) region B.  my4 holds the wave's rows in lanes 0.. and rowb the row of
+    // this lane's region-B chunk.
+    auto issue_part = [&](int t, int m, int32_t my4, int32_t rowb) {
         const uint32_t buf = ring_base + uint32_t((t % kRing) * G::kTileBytes);
-        if (m < G::kRowsPerWaveA) {
-            const int r = wave * 8 + m;
-            const int32_t row = __builtin_amdgcn_readlane(my8, m);
+        if (m < my_rows) {
+            const int r = row_base + m;
+            const int32_t row = __builtin_amdgcn_readlane(my4, m);
             const uint16_t* src = a.kpool + int64_t(row < 0 ? 0 : row) * DK;   // uniform
             load_lds16_s(src, uint32_t(swz_a(r, a_src_chunk) * 16),
                          __builtin_amdgcn_readfirstlane(buf + uint32_t(r * G::kRowBytesA)));
         } else {
             const uint16_t* srcb = a.kpool + int64_t(rowb < 0 ? 0 : rowb) * DK + b_src_el;
-            load_lds16(srcb, __builtin_amdgcn_readfirstlane(buf + uint32_t(G::kBytesA + wave * 1024)));
+            load_lds16(srcb, __builtin_amdgcn_readfirstlane(buf + uint32_t(G::kBytesA + grp * 1024)));
         }
     };
-    auto tile_rows = [&](int t, int32_t& my8, int32_t& rowb) {
-        my8 = rows[t * kTile + wave * 8 + (lane & 7)];
-        rowb = rows[t * kTile + b_row];
+    auto tile_rows = [&](int t, int32_t& my4, int32_t& rowb) {
+        my4 = rows[t * kTile + row_base + (lane & 7) % my_rows];
+        rowb = is_qk ? 0 : rows[t * kTile + b_row];
     };
     auto issue_tile = [&](int t) {
-        int32_t my8, rowb;
-        tile_rows(t, my8, rowb);
-#pragma unroll
-        for (int m = 0; m < kLoadsPerWave; ++m) issue_part(t, m, my8, rowb);
+        int32_t my4, rowb;
+        tile_rows(t, my4, rowb);
+        for (int m = 0; m < my_loads; ++m) issue_part(t, m, my4, rowb);
     };
-    // A tile issued inside the loop is spread over the iteration: loads kQkLoads[..] after
-    // the QK k-steps listed, the rest after PV output groups, so that the load queue drains
-    // steadily instead of stalling the wave on a burst.
-    int32_t pend_t = -1, pend_my8 = 0, pend_rowb = 0;   // the tile being issued (uniform)
-
-    // Softmax reference: the probabilities are exp2(logit - m_ref) with m_ref fixed at the first
-    // tile where the head has a valid token, never rescaled.  Any reference gives the same
-    // softmax as long as exp2 cannot overflow, so a tile whose max exceeds m_ref by more than
-    // kHeadroom (2^32) switches the whole workgroup to a scan that only tracks the true max;
-    // the split is then computed again with m_ref = that max.  Inputs whose logits stay within
-    // 2^32 of the first tile's max take one pass.
-    float m_seen = -INFINITY;  // max logit (log2 units) over the tiles scanned so far
-
-    // Softmax of one tile as a sequence of small stages, so that they can be slotted between
-    // the QK MFMAs of the next tile: the matrix cores work while the vector ALUs run these.
-    // State of the tile being normalised:
-    float sx[8];                 // scaled logits, then probabilities
-    float stmax = -INFINITY, spsum = 0.f;
-    bool sviol = false;
-    float m_use = 0.f;           // m_ref, or 0 while it is unset
-    uint32_t phi_w[4], plo_w[4];
-    bool scan = false;           // uniform; the workgroup is only tracking the max
-    auto soft_stage = [&](int st, const f32x4 (&sc)[2], uint64_t live) {
-        if (st == 0 || st == 1) {
-            if (uint32_t(live) == 0xffffffffu) {   // uniform: every token of the tile present
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float x = sc[st][r] * a.scale_log2;
-                    sx[4 * st + r] = x;
-                    stmax = fmaxf(stmax, x);
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tok = st * 16 + g16 * 4 + r;
-                    const float x = ((live >> tok) & 1) ? sc[st][r] * a.scale_log2 : -INFINITY;
-                    sx[4 * st + r] = x;
-                    stmax = fmaxf(stmax, x);
-                }
-            }
-        } else if (st == 2) {
-            stmax = max4groups(stmax);
-            m_seen = fmaxf(m_seen, stmax);
-            if (m_ref == -INFINITY) m_ref = stmax;   // first tile with a valid token for the head
-            sviol = stmax > m_ref + kHeadroom;
-            // exp2(-inf - m) = 0 for any finite m; before the head has a reference every
-            // logit of the tile is -inf and any finite m does
-            m_use = m_ref == -INFINITY ? 0.f : m_ref;
-        } else if (st == 3) {
-            if (!scan && __ballot(sviol)) *flag = 1;
-        } else if (st >= 4 && st < 8) {
-            const int i = 2 * (st - 4);
-            sx[i] = __builtin_amdgcn_exp2f(sx[i] - m_use);
-            sx[i + 1] = __builtin_amdgcn_exp2f(sx[i + 1] - m_use);
-            spsum += sx[i] + sx[i + 1];
-        } else if (st >= 8 && st < 12) {
-            // B operand of PV: P^T[kappa][head], kappa = 8*g16 + i <-> token (i < 4 ? 4*g16 + i :
-            // 16 + 4*g16 + i - 4), i.e. sx[i] in order; split into bf16 hi + lo
-            const int e = st - 8;
-            const uint32_t h = pack_bf16(sx[2 * e], sx[2 * e + 1]);
-            phi_w[e] = h;
-            plo_w[e] = pack_bf16(sx[2 * e] - __uint_as_float(h << 16),
-                                 sx[2 * e + 1] - __uint_as_float(h & 0xffff0000u));
+    // wait until this wave's loads of a tile have landed, `later` tiles having been issued
+    // after it
+    auto wait_tile = [&](int later) {
+        if (is_qk) {
+            if (later >= 2) wait_vm<2 * kLoadsQK>();
+            else if (later == 1) wait_vm<kLoadsQK>();
+            else wait_vm<0>();
+        } else {
+            if (later >= 2) wait_vm<2 * kLoadsPV>();
+            else if (later == 1) wait_vm<kLoadsPV>();
+            else wait_vm<0>();
         }
     };
-    constexpr int kStages = 12;
-    auto soft_reset = [&]() {
-        stmax = -INFINITY;
-        spsum = 0.f;
-        sviol = false;
-    };
+
+    bool scan = false;           // uniform; the workgroup is only tracking the max
 
     // S^T = K Q^T for one tile: two 16-token blocks x 16 heads.  Operand reads run kQkAhead
-    // k-steps ahead of the MFMAs (a register ring).  When `prev` is set, softmax stage ks of the
-    // previous tile runs after the MFMAs of k-step ks.  The scheduling fences keep the compiler
-    // from regrouping the pieces.
-    auto qk_tile = [&](const unsigned char* tile, f32x4 (&s)[2], bool with_soft,
-                       const f32x4 (&sc)[2], uint64_t live) {
+    // k-steps ahead of the MFMAs; this wave's loads of tile pend_t go after k-steps 1, 5, 9, 13.
+    auto qk_tile = [&](const unsigned char* tile, f32x4 (&s)[2], int pend_t, int32_t my4, int32_t rowb) {
         s[0] = s[1] = f32x4{0.f, 0.f, 0.f, 0.f};
         uint4 kv[kQkAhead][2];
         auto qk_read = [&](int ks, uint4 (&dst)[2]) {
@@ -349,18 +302,78 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
             const bf16x8 qb = as_bf16x8(qreg[ks]);
             s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks % kQkAhead][0]), qb, s[0], 0, 0, 0);
             s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[ks % kQkAhead][1]), qb, s[1], 0, 0, 0);
-            if (with_soft && ks < kStages) soft_stage(ks, sc, live);
-            if ((ks & 3) == 1 && pend_t >= 0) issue_part(pend_t, ks >> 2, pend_my8, pend_rowb);
+            if ((ks & 1) == 1 && (ks >> 1) < kLoadsQK && pend_t >= 0) issue_part(pend_t, ks >> 1, my4, rowb);
             __builtin_amdgcn_sched_barrier(0);
             if (ks + kQkAhead < KS) qk_read(ks + kQkAhead, kv[ks % kQkAhead]);
         }
     };
 
-    // O^T += V^T P^T over one tile's 32 tokens.  A operand: V^T[d][kappa] via the transpose
-    // load (in each 16-lane group, lane i points at row k0 + i/4, dims n0 + 4*(i%4) .. +3; lane j
-    // receives rows k0..k0+3 of dim n0 + j).  Groups of 4 output blocks: group g+1 is read while
-    // group g's MFMAs issue (fenced so the compiler keeps the two-stage ring).
-    auto pv_tile = [&](const unsigned char* tile, const bf16x8& phi, const bf16x8& plo) {
+    // Softmax of one tile against the fixed reference (first tile with a valid token; a tile
+    // more than kHeadroom above it requests a rescan with the true max).  Produces P^T as the
+    // PV B operand, split into bf16 hi + lo: kappa = 8*g16 + i <-> token (i < 4 ? 4*g16 + i :
+    // 16 + 4*g16 + i - 4).
+    auto softmax = [&](const f32x4 (&sc)[2], uint64_t live, uint4& ph, uint4& pl) {
+        float x[8];
+        float tmax = -INFINITY;
+        if (uint32_t(live) == 0xffffffffu) {   // uniform: every token of the tile present
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                x[i] = sc[i >> 2][i & 3] * a.scale_log2;
+                tmax = fmaxf(tmax, x[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int tok = (i >> 2) * 16 + g16 * 4 + (i & 3);
+                x[i] = ((live >> tok) & 1) ? sc[i >> 2][i & 3] * a.scale_log2 : -INFINITY;
+                tmax = fmaxf(tmax, x[i]);
+            }
+        }
+        tmax = max4groups(tmax);
+        m_seen = fmaxf(m_seen, tmax);
+        if (m_ref == -INFINITY) m_ref = tmax;
+        const bool viol = tmax > m_ref + kHeadroom;
+        if (!scan && __ballot(viol)) *flag = 1;
+        // exp2(-inf - m) = 0 for any finite m; before the head has a reference every logit of
+        // the tile is -inf and any finite m does
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            x[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+            psum += x[i];
+        }
+        l_run += psum;
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t h = pack_bf16(x[2 * e], x[2 * e + 1]);
+            hw[e] = h;
+            lw[e] = pack_bf16(x[2 * e] - __uint_as_float(h << 16),
+                              x[2 * e + 1] - __uint_as_float(h & 0xffff0000u));
+        }
+        ph = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        pl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    };
+    uint4* pb_hi = reinterpret_cast<uint4*>(__builtin_assume_aligned(pbuf + grp * kPBytes, 16)) + lane;
+    uint4* pb_lo = pb_hi + 64;
+    // Bounded wait for the group's PV wave to have read `count` P tiles.  The PV wave reads
+    // P(t) right after the barrier that opens iteration t, without waiting on anything else,
+    // so the wait normally passes at once; the bound only guarantees that the wave cannot
+    // hang, and running out of it poisons the head's sum so the output shows NaN.
+    auto wait_seen = [&](int count) {
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+            if (__hip_atomic_load(&pv_seen[grp], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= count)
+                return;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        l_run = __builtin_nanf("");
+    };
+
+    // O^T += V^T P^T over one tile's 32 tokens (LDS transpose reads, groups of 4 output blocks
+    // read one group ahead); this wave's loads of tile pend_t go after output groups 1 .. 5.
+    auto pv_tile = [&](f32x4 (&acc)[DB], const unsigned char* tile, const bf16x8& phi, const bf16x8& plo, int pend_t,
+                       int32_t my4, int32_t rowb) {
         bf16x8 va[2][4];
         auto pv_read = [&](int db0, bf16x8 (&dst)[4]) {
 #pragma unroll
@@ -377,7 +390,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
         for (int g = 0; g < DB / 4; ++g) {
             __builtin_amdgcn_sched_barrier(0);
             if (g + 1 < DB / 4) pv_read(4 * (g + 1), va[(g + 1) & 1]);
-            if ((g & 1) == 1 && pend_t >= 0) issue_part(pend_t, 5 + (g >> 1), pend_my8, pend_rowb);
+            if (g >= 1 && g <= kLoadsPV && pend_t >= 0) issue_part(pend_t, g - 1, my4, rowb);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -387,107 +400,135 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
                 acc[4 * g + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[g & 1][u], plo, acc[4 * g + u], 0, 0, 0);
         }
     };
+    auto live_mask = [&](int t) {
+        return __ballot(lane < kTile && t * kTile + lane < n && rows[t * kTile + (lane & (kTile - 1))] >= 0);
+    };
 
-    // Softmax reference: the probabilities are exp2(logit - m_ref) with m_ref fixed at the first
-    // tile where the head has a valid token, never rescaled.  Any reference gives the same
-    // softmax as long as exp2 cannot overflow, so a tile whose max exceeds m_ref by more than
-    // kHeadroom (2^32) switches the whole workgroup to a scan that only tracks the true max;
-    // the split is then computed again with m_ref = that max.  Inputs whose logits stay within
-    // 2^32 of the first tile's max take one pass.
-    //
-    // Loop body for tile t: QK of tile t+1 (with tile t's softmax stages in its shadow), then PV
-    // of tile t.
-    for (int pass = 0; pass < 2; ++pass) {
-        scan = false;
-        f32x4 s_cur[2], s_next[2];
-        uint64_t live_cur = 0, live_next = 0;
-        auto live_mask = [&](int t) {
-            return __ballot(lane < kTile && t * kTile + lane < n &&
-                            rows[t * kTile + (lane & (kTile - 1))] >= 0);
-        };
-        for (int t = 0; t < kRing - 1 && t < n_tiles; ++t) issue_tile(t);
-        if (n_tiles > 0) {
-            // tile 0 has landed once at most the later prologue tiles are outstanding
-            const int later = min(kRing - 2, n_tiles - 1);
-            if (later >= 2) wait_vm<2 * kLoadsPerWave>();
-            else if (later == 1) wait_vm<kLoadsPerWave>();
-            else wait_vm<0>();
-            __syncthreads();
-            live_cur = live_mask(0);
-            qk_tile(ring, s_cur, false, s_cur, 0);
-        }
-        for (int t = 0; t < n_tiles; ++t) {
-            soft_reset();
-            if (t + 1 < n_tiles) {
-                // tile t+1 has landed once at most the tiles issued after it are outstanding
-                const int later = min(t + kRing - 2, n_tiles - 1) - (t + 1);
-                if (later >= 1) wait_vm<kLoadsPerWave>();
-                else wait_vm<0>();
-                __syncthreads();   // every wave's part landed; tile t-1's buffer is free again
+    // Pipeline, per tile t: QK waves compute S and P of tile t+1 while PV waves accumulate tile
+    // t with P(t).  The barrier that opens iteration t means: tile t+1 landed, P(t) written,
+    // PV(t-1) done (so tile t-1's buffer takes tile t+3).  A per-group count in LDS tells the
+    // QK wave when its PV wave has read P(t), after which P(t+1) replaces it.  The two roles run separate
+    // copies of the loop with the same sequence of barriers, so that the queries (QK) and the
+    // accumulators (PV) never need registers in the same wave.
+    const int h = h0 + j16;
+    if (is_qk) {
+        const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.hq + h) * DK);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qreg[ks] = qsrc[ks * 4 + g16];
+        wait_vm<0>();
+        for (int pass = 0; pass < 2; ++pass) {
+            scan = false;
+            for (int t = 0; t < kRing - 1 && t < n_tiles; ++t) issue_tile(t);
+            uint4 ph = make_uint4(0, 0, 0, 0), pl = ph;
+            if (n_tiles > 0) {
+                wait_tile(min(kRing - 2, n_tiles - 1));
+                __syncthreads();
+                f32x4 s[2];
+                qk_tile(ring, s, -1, 0, 0);
+                softmax(s, live_mask(0), ph, pl);
+                *pb_hi = ph;
+                *pb_lo = pl;
+            }
+            for (int t = 0; t < n_tiles; ++t) {
+                if (t + 1 < n_tiles) wait_tile(min(t + 2, n_tiles - 1) - (t + 1));
+                __syncthreads();                                       // B_t
                 scan = *flag != 0;
-                pend_t = -1;
+                int pend_t = -1;
+                int32_t my4 = 0, rowb = 0;
                 if (t + kRing - 1 < n_tiles) {
                     pend_t = t + kRing - 1;
-                    tile_rows(pend_t, pend_my8, pend_rowb);
+                    tile_rows(pend_t, my4, rowb);
                 }
-                live_next = live_mask(t + 1);
-                qk_tile(ring + ((t + 1) % kRing) * G::kTileBytes, s_next, true, s_cur, live_cur);
-            } else {
-#pragma unroll
-                for (int st = 0; st < kStages; ++st) soft_stage(st, s_cur, live_cur);
+                if (t + 1 < n_tiles) {
+                    const uint64_t live = live_mask(t + 1);
+                    f32x4 s[2];
+                    qk_tile(ring + ((t + 1) % kRing) * G::kTileBytes, s, pend_t, my4, rowb);
+                    softmax(s, live, ph, pl);
+                    // P(t) must have been read by the group's PV wave before it is replaced
+                    wait_seen(pass * n_tiles + t + 1);
+                    *pb_hi = ph;
+                    *pb_lo = pl;
+                }
             }
-            // In scan mode the products are discarded (the split is computed again), but PV
-            // still runs: skipping it conditionally costs the accumulators their registers.
-            l_run += spsum;
-            pv_tile(ring + (t % kRing) * G::kTileBytes,
-                    as_bf16x8(make_uint4(phi_w[0], phi_w[1], phi_w[2], phi_w[3])),
-                    as_bf16x8(make_uint4(plo_w[0], plo_w[1], plo_w[2], plo_w[3])));
-            s_cur[0] = s_next[0];
-            s_cur[1] = s_next[1];
-            live_cur = live_next;
+            wait_vm<0>();
+            __syncthreads();                 // a flag raised on the last tile is visible
+            if (*flag == 0) break;           // uniform
+            // second pass with the true max as the reference
+            m_ref = m_seen;
+            l_run = 0.f;
+            __syncthreads();                 // everyone has read the flag
+            if (tid == 0) *flag = 0;
+            __syncthreads();
         }
-        wait_vm<0>();
-        __syncthreads();                 // a flag raised on the last tile is visible
-        if (*flag == 0) break;           // uniform
-        // second pass with the true max as the reference
-        m_ref = m_seen;
-        l_run = 0.f;
-#pragma unroll
-        for (int i = 0; i < DB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        __syncthreads();                 // everyone has read the flag
-        if (tid == 0) *flag = 0;
-        __syncthreads();
-    }
-
-    // full row sum of head h0 + j16 across the four lane groups
-    const float l_tot = sum4groups(l_run);
-    const int h = h0 + j16;
-    // lane holds O^T[d = db*16 + 4*g16 + r][head h]
-    if (a.splits == 1) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        float* o = a.out + (int64_t(b) * a.hq + h) * DV;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-            *reinterpret_cast<float4*>(o + db * 16 + g16 * 4) =
-                make_float4(acc[db][0] * inv, acc[db][1] * inv, acc[db][2] * inv, acc[db][3] * inv);
-    } else {
-        const int64_t pidx = (int64_t(b) * a.hq + h) * a.splits + s_idx;
-        float* o = a.part_acc + pidx * DV;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-            *reinterpret_cast<float4*>(o + db * 16 + g16 * 4) =
-                make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+        // full row sum of head h across the four lane groups
+        const float l_tot = sum4groups(l_run);
         if (g16 == 0) {
-            // natural-log units, as the combine expects
-            a.part_ml[pidx * 2] = m_ref == -INFINITY ? -INFINITY : m_ref * 0.6931471805599453f;
-            a.part_ml[pidx * 2 + 1] = l_tot;
+            lbuf[(grp * 16 + j16) * 2] = m_ref;
+            lbuf[(grp * 16 + j16) * 2 + 1] = l_tot;
+            if (a.splits > 1) {
+                const int64_t pidx = (int64_t(b) * a.hq + h) * a.splits + s_idx;
+                // natural-log units, as the combine expects
+                a.part_ml[pidx * 2] = m_ref == -INFINITY ? -INFINITY : m_ref * 0.6931471805599453f;
+                a.part_ml[pidx * 2 + 1] = l_tot;
+            }
+        }
+        __syncthreads();
+    } else {
+        f32x4 acc[DB];
+        for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+            for (int i = 0; i < DB; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < kRing - 1 && t < n_tiles; ++t) issue_tile(t);
+            if (n_tiles > 0) {
+                wait_tile(min(kRing - 2, n_tiles - 1));
+                __syncthreads();
+            }
+            for (int t = 0; t < n_tiles; ++t) {
+                if (t + 1 < n_tiles) wait_tile(min(t + 2, n_tiles - 1) - (t + 1));
+                __syncthreads();                                       // B_t
+                int pend_t = -1;
+                int32_t my4 = 0, rowb = 0;
+                if (t + kRing - 1 < n_tiles) {
+                    pend_t = t + kRing - 1;
+                    tile_rows(pend_t, my4, rowb);
+                }
+                const uint4 rh = *pb_hi, rl = *pb_lo;
+                // both reads have returned before the count tells the QK wave
+                __hip_atomic_store(&pv_seen[grp], pass * n_tiles + t + 1, __ATOMIC_RELEASE,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+                pv_tile(acc, ring + (t % kRing) * G::kTileBytes, as_bf16x8(rh), as_bf16x8(rl), pend_t, my4, rowb);
+            }
+            wait_vm<0>();
+            __syncthreads();
+            if (*flag == 0) break;
+            __syncthreads();
+            __syncthreads();
+        }
+        __syncthreads();                     // lbuf written
+        // lane holds O^T[d = db*16 + 4*g16 + r][head h]
+        if (a.splits == 1) {
+            const float l_tot = lbuf[(grp * 16 + j16) * 2 + 1];
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            float* o = a.out + (int64_t(b) * a.hq + h) * DV;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                *reinterpret_cast<float4*>(o + db * 16 + g16 * 4) =
+                    make_float4(acc[db][0] * inv, acc[db][1] * inv, acc[db][2] * inv, acc[db][3] * inv);
+        } else {
+            const int64_t pidx = (int64_t(b) * a.hq + h) * a.splits + s_idx;
+            float* o = a.part_acc + pidx * DV;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                *reinterpret_cast<float4*>(o + db * 16 + g16 * 4) =
+                    make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
         }
     }
 }
 
 template <int DK, int DV>
 size_t mfma_smem(int chunk) {
-    return size_t(kRing) * Geo<DK, DV>::kTileBytes + size_t(chunk + 4) * sizeof(int32_t);
+    return size_t(kRing) * Geo<DK, DV>::kTileBytes + size_t(kGroups) * kPBytes +
+           size_t(2 * kGroups * 16) * sizeof(float) + size_t(chunk + 4 + kGroups) * sizeof(int32_t);
 }
 
 }  // namespace
@@ -501,13 +542,16 @@ bool mfma_latent_applicable(const tsa_kv_pool& pool, const tsa_decode_params& p)
     if (!d.v_from_k || d.head_dim_k != 576 || d.head_dim_v != 512 || d.num_kv_heads != 1) return false;
     if (p.num_q_heads != 64) return false;
     if (pool.slots() >= (int64_t(1) << 31)) return false;   // slots kept as 32-bit in LDS
-    return mfma_smem<576, 512>(int(ceil_div(p.top_k, kTile)) * kTile) <= 160 * 1024;
+    int splits = 0;
+    const int chunk = mfma_latent_chunk(p, &splits);
+    return chunk <= kMaxChunk && mfma_smem<576, 512>(chunk) <= 160 * 1024;
 }
 
 int mfma_latent_chunk(const tsa_decode_params& p, int* splits) {
     const int tiles = int(ceil_div(p.top_k, kTile));
     int s = int(ceil_div(256, std::max(p.batch, 1)));   // one workgroup per CU
     s = std::max(1, std::min({s, tiles, 64}));   // the combine takes at most 64 splits
+    s = std::max(s, int(ceil_div(tiles, kMaxChunk / kTile)));   // the row list fits in LDS
     const int chunk = int(ceil_div(tiles, s)) * kTile;
     *splits = int(ceil_div(p.top_k, chunk));
     return chunk;
@@ -541,7 +585,7 @@ hipError_t launch_attention_mfma(const tsa_kv_pool& pool, int layer, const tsa_d
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
     if (e != hipSuccess) return e;
-    dim3 grid(plan.splits, p.num_q_heads / (kWaves * 16), p.batch);
+    dim3 grid(plan.splits, p.num_q_heads / (kGroups * 16), p.batch);
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, s, a);
     return hipGetLastError();
 }

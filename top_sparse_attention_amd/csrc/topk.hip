@@ -9,7 +9,10 @@
 // interleaved copies so that lanes hitting the same bin spread over distinct addresses).  A pass
 // also finds the smallest and largest candidate key; when they are equal the threshold key is
 // known and the remaining passes are skipped (ties at the threshold are common for
-// integer-valued scores).  After the passes, every element whose key exceeds the threshold is
+// integer-valued scores).  The pass is latency-bound, so it keeps workgroup barriers few: the
+// histogram and the key-range slots are double-buffered by pass parity (the next pass's copy
+// is cleared during the current one), and the wave-level scans and min / max use DPP lane
+// moves rather than LDS round trips.  After the passes, every element whose key exceeds the threshold is
 // kept, and of the elements equal to it the lowest positions fill the rest; one block-wide
 // scan over positions (each thread owns a contiguous run) of the packed counts (above,
 // equal) yields both the tie ranks and the output offsets, so the output comes out ascending
@@ -27,34 +30,65 @@ __device__ inline uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// DPP lane move: lanes whose source falls outside the pattern (or a disabled row) read 0.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint32_t dpp0(uint32_t x) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(x), CTRL, ROWS, 0xf, false));
+}
+
+// Inclusive prefix sum over the wave in lane order (modulo 2^32): shifts within each row of
+// 16 lanes, then the last lane of row 0 and of row 1 carried into the rows above.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+    x += dpp0<0x111>(x);          // row_shr:1
+    x += dpp0<0x112>(x);          // row_shr:2
+    x += dpp0<0x114>(x);          // row_shr:4
+    x += dpp0<0x118>(x);          // row_shr:8
+    x += dpp0<0x142, 0xa>(x);     // row_bcast:15 into rows 1 and 3
+    x += dpp0<0x143, 0xc>(x);     // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// min / max over the wave (every lane gets the result): rotations within each row of 16
+// lanes, then the cross-row lane swaps
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+    x = min(x, uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x128, 0xf, 0xf, false)));
+    x = min(x, uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x124, 0xf, 0xf, false)));
+    x = min(x, uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x122, 0xf, 0xf, false)));
+    x = min(x, uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x121, 0xf, 0xf, false)));
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = min(a[0], a[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return min(c[0], c[1]);
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+    x = max(x, uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x128, 0xf, 0xf, false)));
+    x = max(x, uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x124, 0xf, 0xf, false)));
+    x = max(x, uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x122, 0xf, 0xf, false)));
+    x = max(x, uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x121, 0xf, 0xf, false)));
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = max(a[0], a[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return max(c[0], c[1]);
+}
+
 // Exclusive scan over the block in thread order; returns this thread's prefix, total in *total.
+// sh_waves holds 2 * kWaves + 1 ints; callers alternate between two such areas so that one
+// call's reads never race the next call's writes.
 __device__ inline int block_exclusive_scan(int v, int* sh_waves, int* total) {
     // sums wrap modulo 2^32 (unsigned arithmetic): packed counts rely on it
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = uint32_t(v);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = uint32_t(__shfl_up(int(x), o));
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_inclusive_sum(uint32_t(v));
     if (lane == 63) sh_waves[wave] = int(x);
     __syncthreads();
     if (threadIdx.x < 64) {
         const uint32_t w = threadIdx.x < kWaves ? uint32_t(sh_waves[threadIdx.x]) : 0u;
-        uint32_t s = w;
-#pragma unroll
-        for (int o = 1; o < kWaves; o <<= 1) {
-            const uint32_t y = uint32_t(__shfl_up(int(s), o));
-            if ((int)threadIdx.x >= o) s += y;
-        }
+        const uint32_t s = wave_inclusive_sum(w);
         if (threadIdx.x < kWaves) sh_waves[kWaves + threadIdx.x] = int(s - w);
         if (threadIdx.x == kWaves - 1) sh_waves[2 * kWaves] = int(s);
     }
     __syncthreads();
-    const int r = int(uint32_t(sh_waves[kWaves + wave]) + x - uint32_t(v));
     *total = sh_waves[2 * kWaves];
-    __syncthreads();
-    return r;
+    return int(uint32_t(sh_waves[kWaves + wave]) + x - uint32_t(v));
 }
 
 template <int IPT>
@@ -63,10 +97,10 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
                                                               const int32_t* __restrict__ seq_lens,
                                                               int max_len, int k,
                                                               int32_t* __restrict__ out) {
-    __shared__ uint32_t hist[256 * kCopies];
-    __shared__ int sh_scan[2 * kWaves + 1];
+    __shared__ uint32_t hist[2][256 * kCopies];    // one buffer per pass parity
+    __shared__ int sh_scan[2][2 * kWaves + 1];
     __shared__ int sh_sel[4];
-    __shared__ uint32_t sh_mm[2];
+    __shared__ uint32_t sh_mm[4];                  // candidate key range, per pass parity
 
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
@@ -103,38 +137,43 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
 
     uint32_t prefix = 0, mask = 0;
     int remaining = k;  // how many of the elements matching `prefix` under `mask` to keep
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256 * kCopies; i += kThreads) hist[i] = 0;
-        if (tid == 0) {
-            sh_mm[0] = 0xffffffffu;
-            sh_mm[1] = 0u;
-        }
-        __syncthreads();
+    for (int i = tid; i < 256 * kCopies; i += kThreads) hist[0][i] = 0;
+    if (tid == 0) {
+        sh_mm[0] = 0xffffffffu;
+        sh_mm[1] = 0u;
+    }
+    __syncthreads();
+    int pass = 0;
+    for (int shift = 24; shift >= 0; shift -= 8, ++pass) {
+        uint32_t* h = hist[pass & 1];
+        // the other buffer was last read before the previous pass's selection barrier
+        for (int i = tid; i < 256 * kCopies; i += kThreads) hist[(pass + 1) & 1][i] = 0;
         const int copy = tid & (kCopies - 1);
         uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
         for (int i = 0; i < IPT; ++i) {
             if (base + i < len && (key[i] & mask) == prefix) {
-                atomicAdd(&hist[((key[i] >> shift) & 255u) * kCopies + copy], 1u);
+                atomicAdd(&h[((key[i] >> shift) & 255u) * kCopies + copy], 1u);
                 kmin = min(kmin, key[i]);
                 kmax = max(kmax, key[i]);
             }
         }
         // candidates' key range: once they are all equal, the k-th key is known exactly
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-            kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-        }
+        kmin = wave_min(kmin);
+        kmax = wave_max(kmax);
         if ((tid & 63) == 0) {
-            atomicMin(&sh_mm[0], kmin);
-            atomicMax(&sh_mm[1], kmax);
+            atomicMin(&sh_mm[2 * (pass & 1)], kmin);
+            atomicMax(&sh_mm[2 * (pass & 1) + 1], kmax);
+        }
+        // the next pass's range slots start empty (last read before this pass began)
+        if (tid == 0) {
+            sh_mm[2 * ((pass + 1) & 1)] = 0xffffffffu;
+            sh_mm[2 * ((pass + 1) & 1) + 1] = 0u;
         }
         __syncthreads();
-        if (sh_mm[0] == sh_mm[1]) {      // uniform
-            prefix = sh_mm[0];
+        if (sh_mm[2 * (pass & 1)] == sh_mm[2 * (pass & 1) + 1]) {      // uniform
+            prefix = sh_mm[2 * (pass & 1)];
             mask = 0xffffffffu;
-            __syncthreads();
             break;
         }
         // bins in descending digit order: thread j < 256 owns digit 255 - j
@@ -142,10 +181,10 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
         if (tid < 256) {
             const int dgt = 255 - tid;
 #pragma unroll
-            for (int j = 0; j < kCopies; ++j) c += hist[dgt * kCopies + ((j + tid) & (kCopies - 1))];
+            for (int j = 0; j < kCopies; ++j) c += h[dgt * kCopies + ((j + tid) & (kCopies - 1))];
         }
         int total;
-        const int above = block_exclusive_scan(c, sh_scan, &total);  // count with a larger digit
+        const int above = block_exclusive_scan(c, sh_scan[pass & 1], &total);  // count with a larger digit
         if (tid < 256 && above < remaining && above + c >= remaining) {
             sh_sel[0] = 255 - tid;
             sh_sel[1] = remaining - above;
@@ -174,7 +213,7 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
         eq += (v && m == prefix);
     }
     int total;
-    const uint32_t packed = uint32_t(block_exclusive_scan(int((uint32_t(gt) << 16) | uint32_t(eq)), sh_scan, &total));
+    const uint32_t packed = uint32_t(block_exclusive_scan(int((uint32_t(gt) << 16) | uint32_t(eq)), sh_scan[pass & 1], &total));
     const int gt_before = int(packed >> 16), eq_before = int(packed & 0xffffu);
     // output offset: every earlier element above, plus the earlier equal ones that are kept
     int off = gt_before + min(eq_before, remaining);

@@ -266,6 +266,63 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(const float* _
     }
 }
 
+// The same merge for at most kSmallSplits splits, as one pass with no barrier: every thread
+// first issues its loads of all the splits' accumulators, then reads the (max, sum) pairs (the
+// same few addresses for the whole workgroup) and computes the split weights in registers
+// while those loads are in flight.
+constexpr int kSmallSplits = 8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4v;
+
+__device__ __forceinline__ float4 load_nt_f4(const float4* p) {
+    const f32x4v v = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+__global__ void __launch_bounds__(kCombineThreads) combine_small_kernel(const float* __restrict__ part_ml,
+                                                                        const float* __restrict__ part_acc,
+                                                                        int splits, int dv,
+                                                                        float* __restrict__ out) {
+    const int bh = blockIdx.x;  // b * Hq + h
+    const float4* acc = reinterpret_cast<const float4*>(part_acc + int64_t(bh) * splits * dv);
+    float4* o = reinterpret_cast<float4*>(out + int64_t(bh) * dv);
+    const int dv4 = dv >> 2;
+    const float* ml = part_ml + int64_t(bh) * splits * 2;
+    float w[kSmallSplits];
+    bool have_w = false;
+    for (int d = threadIdx.x; d < dv4; d += kCombineThreads) {
+        float4 v[kSmallSplits];
+#pragma unroll
+        for (int sp = 0; sp < kSmallSplits; ++sp)
+            v[sp] = sp < splits ? load_nt_f4(acc + int64_t(sp) * dv4 + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+        if (!have_w) {
+            float m[kSmallSplits], M = -INFINITY;
+#pragma unroll
+            for (int sp = 0; sp < kSmallSplits; ++sp) {
+                m[sp] = sp < splits ? ml[2 * sp] : -INFINITY;
+                M = fmaxf(M, m[sp]);
+            }
+            float L = 0.f;
+#pragma unroll
+            for (int sp = 0; sp < kSmallSplits; ++sp) {
+                w[sp] = m[sp] == -INFINITY ? 0.f : __expf(m[sp] - M);
+                L += sp < splits ? ml[2 * sp + 1] * w[sp] : 0.f;
+            }
+#pragma unroll
+            for (int sp = 0; sp < kSmallSplits; ++sp) w[sp] = L > 0.f ? w[sp] / L : 0.f;
+            have_w = true;
+        }
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int sp = 0; sp < kSmallSplits; ++sp) {
+            x.x = fmaf(v[sp].x, w[sp], x.x);
+            x.y = fmaf(v[sp].y, w[sp], x.y);
+            x.z = fmaf(v[sp].z, w[sp], x.z);
+            x.w = fmaf(v[sp].w, w[sp], x.w);
+        }
+        o[d] = x;
+    }
+}
+
 size_t valu_smem_bytes(int T, int G, int dk, int dv, bool alias) {
     size_t s = size_t(G) * dk * 2 + size_t(T) * (dk + 8) * 2;
     if (!alias) s += size_t(T) * (dv + 8) * 2;
@@ -404,8 +461,12 @@ hipError_t launch_attention(const tsa_kv_pool& pool, int layer, const tsa_decode
         e = launch_valu(a, pool, p, plan, s);
     }
     if (e != hipSuccess || plan.splits == 1) return e;
-    hipLaunchKernelGGL(combine_kernel, dim3(p.batch * p.num_q_heads), dim3(kCombineThreads), 0, s,
-                       a.part_ml, a.part_acc, plan.splits, d.head_dim_v, out);
+    if (plan.splits <= kSmallSplits)
+        hipLaunchKernelGGL(combine_small_kernel, dim3(p.batch * p.num_q_heads), dim3(kCombineThreads), 0, s,
+                           a.part_ml, a.part_acc, plan.splits, d.head_dim_v, out);
+    else
+        hipLaunchKernelGGL(combine_kernel, dim3(p.batch * p.num_q_heads), dim3(kCombineThreads), 0, s,
+                           a.part_ml, a.part_acc, plan.splits, d.head_dim_v, out);
     return hipGetLastError();
 }
 

@@ -213,12 +213,15 @@ def bench_tier(args):
         for i in range(0, flat.numel(), block.numel()):
             n = min(block.numel(), flat.numel() - i)
             flat[i:i + n].copy_(block[:n])
-    cache = KvPool(C, P, w.num_kv_heads, w.head_dim_k, w.head_dim_v)
-    tier = LruTier(cache, NL, R, npr, host_k, host_v)
-    # initial state: the last quarter of every (layer, request)'s pages, in key order
-    keep = max(1, npr // 4)
-    pre = np.array([(l * R + r) * npr + p for l in range(NL) for r in range(R) for p in range(npr - keep, npr)],
-                   dtype=np.int64)[:C]
+    # the cache unit: whole pages, or single token rows (a pool of one-token pages holding the
+    # same bytes); the host copy is the same either way
+    CP, UP, unpr = (C, P, npr) if args.tier_unit == "page" else (C * P, 1, npr * P)
+    cache = KvPool(CP, UP, w.num_kv_heads, w.head_dim_k, w.head_dim_v)
+    tier = LruTier(cache, NL, R, unpr, host_k, host_v)
+    # initial state: the last quarter of every (layer, request)'s pages (or tokens), in key order
+    keep = max(1, unpr // 4)
+    ar = np.arange(unpr - keep, unpr, dtype=np.int64)
+    pre = np.concatenate([(l * R + r) * unpr + ar for l in range(NL) for r in range(R)])[:CP]
     tier.preload(pre)
     params = decode_params(R, w.num_q_heads, k, L, w.sm_scale)
     ws = torch.empty(max(workspace_bytes(cache, params), 256), dtype=torch.uint8, device="cuda")
@@ -239,19 +242,25 @@ def bench_tier(args):
     pos_dev = [[torch.from_numpy(a).cuda() for a in lp] for lp in pos_all]
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
-    table_dev = [torch.empty((R, npr), dtype=torch.int32, device="cuda") for _ in range(2)]
+    table_dev = [torch.full((R, unpr), -1, dtype=torch.int32, device="cuda") for _ in range(2)]
     fetched = [torch.cuda.Event() for _ in range(2)]
     done = {}
     ev_attn = []
+    host_s = {"plan": 0.0, "fetch": 0.0}
     gidx = 0
 
     def run_step(step, timed):
         nonlocal gidx
         for layer in range(NL):
-            table, _ = tier.plan(layer, gidx, pos_all[step][layer])
+            h0 = time.perf_counter()
+            tier.plan(layer, gidx, pos_all[step][layer], table=False)
+            h1 = time.perf_counter()
             if gidx - 2 in done:
                 side.wait_event(done[gidx - 2])
-            tier.fetch(table, table_dev[gidx & 1], stream=side)
+            tier.fetch(table_dev[gidx & 1], stream=side)
+            if timed:
+                host_s["plan"] += h1 - h0
+                host_s["fetch"] += time.perf_counter() - h1
             fetched[gidx & 1].record(side)
             main.wait_event(fetched[gidx & 1])
             e0 = torch.cuda.Event(enable_timing=True) if timed else None
@@ -283,16 +292,19 @@ def bench_tier(args):
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_attn]))
     ms_step = elapsed * 1e3 / args.steps
     res = {
-        "metric": "tiered sparse decode tokens/s (8 layers per token) and HBM page-cache hit rate",
+        "metric": "tiered sparse decode tokens/s (8 layers per token) and HBM cache hit rate",
         "value": round(R / (ms_step * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "requests": R, "context": L, "layers": NL, "top_k": k,
-                   "page_size": P, "cache_pages": C, "logical_pages": keys, "q_heads": w.num_q_heads,
+                   "page_size": P, "cache_unit": args.tier_unit, "cache_slots": CP,
+                   "cache_bytes": CP * UP * row * 4, "logical_pages": keys, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim": w.head_dim_k, "parallelism": "none"},
         "tier": {"hit_rate": round(hits / max(hits + misses, 1), 4), "hits": hits, "misses": misses,
                  "h2d_GBps": round(h2d / elapsed / 1e9, 2), "h2d_bytes_per_step": h2d // args.steps,
-                 "attention_ms_per_layer": round(attn_ms, 4)},
+                 "attention_ms_per_layer": round(attn_ms, 4),
+                 "host_plan_ms_per_step": round(host_s["plan"] * 1e3 / args.steps, 3),
+                 "host_fetch_call_ms_per_step": round(host_s["fetch"] * 1e3 / args.steps, 3)},
     }
     print(json.dumps(res), flush=True)
 
@@ -308,6 +320,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--tier-requests", type=int, default=16,
                     help="requests of the tiered workload (the full 256 needs 128 GiB of pinned memory)")
+    ap.add_argument("--tier-unit", choices=("page", "token"), default="page",
+                    help="cache unit of the tiered workload: whole pages or single token rows")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run a plain streaming copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),

@@ -229,7 +229,10 @@ tsa_status tsa_sparse_decode_attn(tsa_kv_pool* pool, int32_t layer, const tsa_de
  * The cache is an ordinary pool (num_layers 1, num_pages = cache slots, no indexer region);
  * a pool created without device regions gives a bookkeeping-only tier (plan, release, stats;
  * host_k / host_v may then be NULL and fetch is refused);
- * a slot holds one page of any (layer, request).  Logical page keys are
+ * a slot holds one page of any (layer, request).  The cache pool's page size is the unit of
+ * caching: pages of P tokens cache whole pages; a pool with page_size 1 and pages_per_req =
+ * the request length caches single token rows, which is what the HiSparse paragraph loads on a
+ * miss.  The host copy is the same bytes either way.  Logical page keys are
  *     key = (layer * num_req + req) * pages_per_req + page.
  * host_k / host_v: pinned host memory (hipHostMalloc, e.g. torch pin_memory=True), key-major:
  * page `key` occupies bytes [key * page_bytes, (key + 1) * page_bytes) with
@@ -260,9 +263,10 @@ tsa_status tsa_lru_destroy(tsa_lru* lru);
 tsa_status tsa_lru_preload(tsa_lru* lru, int64_t n, const int64_t* keys);
 
 /* Host bookkeeping for one layer.  positions: host int32 [n_req][k] token positions (entries
- * < 0 or >= pages_per_req * page_size are ignored).  slot_table: host int32
+ * < 0 or >= pages_per_req * page_size are ignored).  slot_table (nullable): host int32
  * [n_req][pages_per_req], filled with the slot of every touched page and -1 elsewhere (a page
- * table for tsa_sparse_attn_gather on the cache pool, layer 0).  The touched pages are pinned
+ * table for tsa_sparse_attn_gather on the cache pool, layer 0); tsa_lru_fetch writes the same
+ * entries into the device table whether or not it is given.  The touched pages are pinned
  * under `tag`.  n_fetch (nullable) receives the number of page copies now pending.  Fails
  * with TSA_ERR_CAPACITY, changing nothing, if the misses exceed the free slots plus the
  * unpinned pages the plan does not touch. */
@@ -273,11 +277,14 @@ tsa_status tsa_lru_plan(tsa_lru* lru, int32_t layer, int64_t tag, int32_t n_req,
 /* Device workspace for tsa_lru_fetch with up to n_req requests per plan. */
 tsa_status tsa_lru_workspace_bytes(const tsa_lru* lru, int32_t n_req, size_t* bytes);
 
-/* Enqueue on `stream`: the slot table (host, as filled by the last plan) to slot_table_dev
- * (int32 [n_req][pages_per_req]) and the copies of every pending page from host memory into
- * its slot.  The caller orders `stream` after every kernel that reads a page a released tag
- * held (eviction reuses those slots) and orders the attention of the layer after this call
- * (e.g. with events). */
+/* Enqueue on `stream`: the entries the last plan set (the slots of its touched pages) into
+ * slot_table_dev (int32 [n_req][pages_per_req]), and the copies of every pending page from host
+ * memory into its slot.  Entries of pages the plan did not touch are left as they were (an
+ * attention over the plan's positions reads only touched pages), so a fetch moves 12 bytes
+ * per touched page instead of the whole table.  slot_table is not read (the entries come from
+ * the plan; it may be NULL).  n_req must cover the last plan's requests.  The caller orders
+ * `stream` after every kernel that reads a page a released tag held (eviction reuses those
+ * slots) and orders the attention of the layer after this call (e.g. with events). */
 tsa_status tsa_lru_fetch(tsa_lru* lru, int32_t n_req, const int32_t* slot_table,
                          int32_t* slot_table_dev, void* workspace, size_t ws_bytes,
                          void* stream);

@@ -248,6 +248,43 @@ def test_lru_tier_matches_oracle(capacity, K):
         assert st["hits"] > 0 and st["evictions"] > 0      # a cache that both hits and evicts
 
 
+@pytest.mark.parametrize("capacity", [400, 700])
+def test_lru_token_tier_matches_oracle(capacity):
+    """Token-granular tier (a cache pool with one-token pages): slot tables and counters equal
+    the oracle's LRU over token keys.  Up to three tags are in flight and the middle one is
+    released first, so released slots must rejoin the eviction order by touch time, not at
+    the newest end; plans without the host table count the same."""
+    from oracle import lru
+    L, R, T, K = 2, 3, 768, 40
+    cache = _pool(capacity, 1, kv_heads=2, dk=128, dv=128)
+    tier = tsa.LruTier(cache, L, R, T)
+    oc = lru.LRUCache(capacity)
+    rng = np.random.default_rng(capacity + 7)
+    held = []
+    g = 0
+    for step in range(6):
+        for layer in range(L):
+            pos = _tier_positions(rng, R, K, T, hot=2)
+            want_table = g % 3 != 2
+            table, pending = tier.plan(layer, g, pos, table=want_table)
+            ref = lru.plan_layer(oc, layer, R, T, pos, 1, g)
+            if want_table:
+                assert np.array_equal(table, ref), (step, layer)
+            else:
+                assert table is None
+            held.append(g)
+            if len(held) == 3:
+                # release the middle tag, then the oldest: out of plan order
+                for tag in (held[1], held[0]):
+                    tier.release(tag)
+                    oc.release(tag)
+                held = held[2:]
+            g += 1
+            st = tier.stats()
+            assert (st["hits"], st["misses"], st["evictions"]) == (oc.hits, oc.misses, oc.evictions)
+    assert oc.evictions > 0 and oc.hits > 0
+
+
 def test_lru_tier_capacity_error_changes_nothing():
     P, R, NPR = 64, 2, 8
     cache = _pool(4, P, kv_heads=2, dk=128, dv=128)
@@ -276,4 +313,4 @@ def test_lru_tier_refuses_fetch_without_device_memory():
     tier = tsa.LruTier(cache, 1, 1, 4)
     table, _ = tier.plan(0, 0, np.array([[0]], dtype=np.int32))
     with pytest.raises(tsa.TsaError):
-        _lib.call("tsa_lru_fetch", tier.handle, 1, table.ctypes.data_as(_lib.P_i32), None, None, 0, None)
+        _lib.call("tsa_lru_fetch", tier.handle, 1, None, None, None, 0, None)

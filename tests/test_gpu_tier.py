@@ -1,9 +1,10 @@
-"""GPU tests of the tiered KV cache (HBM page cache with LRU eviction over pinned host memory).
+"""GPU tests of the tiered KV cache (HBM cache with LRU eviction over pinned host memory), with
+whole pages and with single token rows as the unit.
 
 A scaled tiered workload (4 requests x 4096 tokens x 8 layers, page 64, 16 query / 2 KV heads,
-d = 128, top-256 seeded locality-biased positions, cache = a quarter of all pages) runs two
-decode steps layer by layer: plan on the host, fetch on a side stream, attention on the main
-stream after the fetch, release of the layer before.  Checked:
+d = 128, top-256 seeded locality-biased positions, cache = a quarter of all pages' bytes) runs
+two decode steps layer by layer: plan on the host, fetch on a side stream, attention on the
+main stream after the fetch, release of the layer before.  Checked, for each unit:
   * slot tables, hits, misses and evictions equal the oracle's LRU under the same sequence;
   * attention through the cache is bit-identical to attention over a pool holding every page
     (tier on vs off);
@@ -50,7 +51,7 @@ def _run_tier(tsa, st, steps):
             # eviction may reuse slots of layers released so far: their attention must be done
             if g - 2 in done:
                 side.wait_event(done[g - 2])
-            st.tier.fetch(table, table_dev[g & 1], stream=side)
+            st.tier.fetch(table_dev[g & 1], stream=side)
             fetched[g & 1].record(side)
             main.wait_event(fetched[g & 1])
             topk = torch.from_numpy(pos).cuda()
@@ -69,11 +70,15 @@ def _run_tier(tsa, st, steps):
     return outs, tables, positions
 
 
-@pytest.fixture(scope="module")
-def tier_run(tsa):
+@pytest.fixture(scope="module", params=["page", "token"])
+def tier_run(tsa, request):
     from top_sparse_attention_amd import workload
     w = synth.get("tiered_b256_64k")
-    st = workload.stage_tier(w, seed=0, num_req=4, length=4096, num_layers=8, top_k=256)
+    # token unit: a cache of 48 pages' bytes (3,072 token slots) so that 2 steps x 8 layers x
+    # 1,024 touched tokens also evict
+    cache_pages = 48 if request.param == "token" else None
+    st = workload.stage_tier(w, seed=0, num_req=4, length=4096, num_layers=8, top_k=256,
+                             cache_pages=cache_pages, unit=request.param)
     outs, tables, positions = _run_tier(tsa, st, steps=2)
     return st, outs, tables, positions
 
@@ -83,14 +88,14 @@ def test_tier_bookkeeping_matches_oracle(tier_run):
     oc = lru.LRUCache(st.cache.desc.num_pages)
     for g, pos in enumerate(positions):
         layer = g % st.w.num_layers
-        ref = lru.plan_layer(oc, layer, st.num_req, st.pages_per_req, pos, st.w.page_size, g)
+        ref = lru.plan_layer(oc, layer, st.num_req, st.pages_per_req, pos, st.cache.desc.page_size, g)
         assert np.array_equal(tables[g], ref), g
         if g > 0:
             oc.release(g - 1)
     s = st.tier.stats()
     assert (s["hits"], s["misses"], s["evictions"]) == (oc.hits, oc.misses, oc.evictions)
     assert s["misses"] > 0 and s["evictions"] > 0
-    page_bytes = st.w.page_size * st.w.num_kv_heads * st.w.head_dim_k * 2
+    page_bytes = st.cache.desc.page_size * st.w.num_kv_heads * st.w.head_dim_k * 2
     assert s["h2d_bytes"] == 2 * page_bytes * s["misses"]
     print(f"tier: hits {s['hits']} misses {s['misses']} evictions {s['evictions']} "
           f"hit rate {s['hits'] / (s['hits'] + s['misses']):.3f}")
@@ -101,7 +106,7 @@ def test_tier_on_equals_tier_off(tsa, tier_run):
     st, outs, tables, positions = tier_run
     w = st.w
     keys = w.num_layers * st.num_req * st.pages_per_req
-    full = tsa.KvPool(keys, w.page_size, w.num_kv_heads, w.head_dim_k, w.head_dim_v)
+    full = tsa.KvPool(keys, st.cache.desc.page_size, w.num_kv_heads, w.head_dim_k, w.head_dim_v)
     full.k.copy_(st.host_k.view(-1).cuda())
     full.v.copy_(st.host_v.view(-1).cuda())
     ws = torch.empty(max(tsa.workspace_bytes(full, st.params), 256), dtype=torch.uint8, device="cuda")

@@ -186,30 +186,31 @@ class LruTier:
         keys = np.ascontiguousarray(keys, dtype=np.int64)
         call("tsa_lru_preload", self.handle, int(keys.shape[0]), keys.ctypes.data_as(_lib.P_i64))
 
-    def plan(self, layer: int, tag: int, positions: np.ndarray):
-        """positions: int32 [n_req, k].  Returns (slot_table int32 [n_req, pages_per_req],
-        pending copies)."""
+    def plan(self, layer: int, tag: int, positions: np.ndarray, table: bool = True):
+        """positions: int32 [n_req, k].  Returns (slot_table int32 [n_req, pages_per_req], or
+        None when ``table`` is false, and the number of pending copies)."""
         positions = np.ascontiguousarray(positions, dtype=np.int32)
         n_req, k = positions.shape
-        table = np.empty((n_req, self.pages_per_req), dtype=np.int32)
+        out = np.empty((n_req, self.pages_per_req), dtype=np.int32) if table else None
         nf = _lib.i64()
         call("tsa_lru_plan", self.handle, int(layer), int(tag), int(n_req), _i32p(positions), int(k),
-             _i32p(table), C.byref(nf))
-        return table, nf.value
+             _i32p(out) if table else None, C.byref(nf))
+        return out, nf.value
 
     def workspace_bytes(self, n_req: int) -> int:
         b = _lib.sz()
         call("tsa_lru_workspace_bytes", self.handle, int(n_req), C.byref(b))
         return b.value
 
-    def fetch(self, table: np.ndarray, table_dev, stream=None):
-        """Upload the slot table and copy the pending pages (enqueued on ``stream``)."""
+    def fetch(self, table_dev, stream=None):
+        """Write the last plan's slots into ``table_dev`` (int32 [n_req, pages_per_req]) and copy
+        the pending pages (enqueued on ``stream``)."""
         import torch
-        table = np.ascontiguousarray(table, dtype=np.int32)
+        n_req = int(table_dev.shape[0])
         if self.workspace is None:
-            self.workspace = torch.empty(max(self.workspace_bytes(table.shape[0]), 256), dtype=torch.uint8,
+            self.workspace = torch.empty(max(self.workspace_bytes(n_req), 256), dtype=torch.uint8,
                                          device=self.cache.k.device)
-        call("tsa_lru_fetch", self.handle, int(table.shape[0]), _i32p(table), _ptr(table_dev),
+        call("tsa_lru_fetch", self.handle, n_req, None, _ptr(table_dev),
              _ptr(self.workspace), _nbytes(self.workspace), _stream(stream))
 
     def release(self, tag: int):

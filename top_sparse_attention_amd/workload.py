@@ -183,10 +183,13 @@ class StagedTier:
 
 def stage_tier(w, seed: int = 0, num_req: Optional[int] = None, length: Optional[int] = None,
                num_layers: Optional[int] = None, top_k: Optional[int] = None,
-               cache_pages: Optional[int] = None, device: str = "cuda") -> StagedTier:
+               cache_pages: Optional[int] = None, unit: str = "page", device: str = "cuda") -> StagedTier:
     """Stage the tiered workload ``w`` (optionally scaled down): fill the pinned host copy of
     every (layer, request) page from ``synth`` and create an empty HBM cache.  The default
-    cache holds ``w.cache_fraction`` of all pages."""
+    cache holds ``w.cache_fraction`` of all pages.  ``unit`` "page" caches whole pages of
+    ``w.page_size`` tokens, "token" single token rows (a cache pool with one-token pages and
+    the same bytes: ``cache_pages`` pages of the workload hold that many times page_size
+    token slots); the host copy is the same either way."""
     import torch
     import synth
     from . import LruTier
@@ -211,6 +214,10 @@ def stage_tier(w, seed: int = 0, num_req: Optional[int] = None, length: Optional
             base = ((layer * R + r) * npr) * P
             hk[base:base + L] = kk.reshape(L, row).view(np.int16)
             hv[base:base + L] = vv.reshape(L, row).view(np.int16)
+    if unit == "token":
+        C, P, npr = C * P, 1, npr * P
+    elif unit != "page":
+        raise ValueError(f"unit must be 'page' or 'token', not {unit!r}")
     cache = KvPool(C, P, w.num_kv_heads, w.head_dim_k, w.head_dim_v, device=device)
     tier = LruTier(cache, NL, R, npr, host_k, host_v)
     q = _dev(synth.queries(w, seed), device)

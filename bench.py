@@ -69,7 +69,7 @@ def cpu_baseline(w, seed: int, budget_s: float = 15.0):
     lens = synth.lens(w, seed)
     qi = synth.index_queries(w, seed)
     q = synth.queries(w, seed)
-    wi = synth.index_weights(w)
+    wi = synth.index_weights(w, seed)
     done, spent, b, passes = 0, 0.0, 0, 0
     while spent < budget_s and b < len(lens):
         L = int(lens[b])
@@ -153,6 +153,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, mib: int):
     doc["_calibration"] = {"copy_bytes_each_way": nbytes, "fetch_kib": float(np.mean(cf)),
                            "write_kib": float(np.mean(cw)), "fetch_scale": round(f_scale, 4),
                            "write_scale": round(w_scale, 4)}
+    doc[f"_calibration/{workload}"] = dict(doc["_calibration"])
     w = None
     try:
         import synth
@@ -170,6 +171,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, mib: int):
         doc[f"{key}/{workload}"] = {
             "kernel": names[0][:120], "src_sha256_16": _src_hash(src),
             "fetch_kib": round(float(fk), 1), "write_kib": round(float(wk), 1),
+            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
             "bytes_per_launch": int(fk * 1024 * f_scale + wk * 1024 * w_scale),
             "read_bytes": int(fk * 1024 * f_scale), "write_bytes": int(wk * 1024 * w_scale)}
     json.dump(doc, open(out_path, "w"), indent=1, sort_keys=True)
@@ -405,6 +407,7 @@ def main():
     lens = st.lens.astype(np.int64)
     D_I = w.index_dim
     idx_bytes = int((lens * (2 * D_I + 4)).sum())
+    idx_flops = float(2 * w.index_heads * D_I * lens.sum())
     n_sel = np.minimum(lens, w.top_k)
     row = w.num_kv_heads * w.head_dim_k * 2 + (0 if w.v_from_k else w.num_kv_heads * w.head_dim_v * 2)
     attn_bytes = int(n_sel.sum() * row + B * w.num_q_heads * w.head_dim_k * 2 +
@@ -440,12 +443,13 @@ def main():
         "config": {"workload": w.name, "requests": B, "context": int(lens.max()),
                    "top_k": w.top_k, "page_size": w.page_size, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim_k": w.head_dim_k, "head_dim_v": w.head_dim_v,
-                   "index_dim": D_I, "parallelism": "none"},
+                   "index_dim": D_I, "index_heads": w.index_heads, "parallelism": "none"},
         "kernels_ms": {"kv_append": round(t_append, 5), "indexer_score": round(t_index, 5),
                        "topk": round(t_topk, 5), "attention": round(t_attn, 5)},
         "kernel_timing": "HIP events between kernels on the launch stream, over a second pass of "
                          "the same steps (the throughput pass has no events between kernels)",
-        "roofline": roof(idx_bytes, t_index, "indexer_score.hip", f"indexer_score/{w.name}"),
+        "roofline": dict(roof(idx_bytes, t_index, "indexer_score.hip", f"indexer_score/{w.name}"),
+                         flops=idx_flops, tflops=round(idx_flops / (t_index * 1e-3) / 1e12, 2)),
         "roofline_attention": dict(roof(attn_bytes, t_attn, attn_src, f"attention/{w.name}"),
                                    flops=attn_flops,
                                    tflops=round(attn_flops / (t_attn * 1e-3) / 1e12, 2)),

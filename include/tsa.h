@@ -169,7 +169,9 @@ tsa_status tsa_kv_append(tsa_kv_pool* pool, int32_t layer, int32_t n_tok, const 
 typedef struct tsa_decode_params {
     int32_t batch;        /* requests B */
     int32_t num_q_heads;  /* Hq, a multiple of the pool's num_kv_heads */
-    int32_t index_heads;  /* H_I >= 1 (ignored by tsa_sparse_attn_gather) */
+    int32_t index_heads;  /* H_I: 1..64 when pages hold >= 16 tokens and index_dim is 32..256
+                             (2..64 heads run on the matrix cores), else 1..8; ignored by
+                             tsa_sparse_attn_gather.  Others give TSA_ERR_UNSUPPORTED. */
     int32_t top_k;        /* k >= 1 */
     int32_t max_len;      /* >= every seq_len; sizes the score buffer */
     float sm_scale;       /* logit scale, e.g. 1/sqrt(head_dim_k) */

@@ -29,6 +29,12 @@ Workloads (the shapes the pages discuss, with synthetic values):
 * ``prefix_b128_16k`` 128 requests sharing a 16384-token prefix plus a private
                      U[1024, 4096]-token suffix (paged-KV page, section "Chia
                      sẻ trang").  32 q heads / 8 KV heads, d=128.
+* ``mla_b64_32k_ih64`` the 64 x 32k latent workload with a 64-head indexer
+                     query (one indexer head per attention head) and integer
+                     head weights in [-2, 3] (lightning-indexer paragraph: many
+                     query heads, one key head, a weighted sum of per-head ReLU
+                     logits).  Scores stay exact in fp32: |score| <= 64 x 3 x
+                     128 x 4 x 4 = 393,216 < 2^24.
 * ``tiered_b256_64k`` 256 requests x 65536 tokens x 8 layers; the HBM page
                      cache holds a quarter of the pages (GLM5.3 sparse-attention
                      page, HiSparse paragraph).  Positions come from a seeded
@@ -43,13 +49,13 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get", "f32_to_bf16_bits", "lens", "free_order",
-    "prefix_groups", "index_queries", "index_weights", "queries",
+    "prefix_groups", "index_queries", "index_weights", "index_inputs", "queries",
     "request_tokens", "tier_positions",
 ]
 
 # stream ids: one independent generator per kind of draw
 _S_LENS, _S_FREE, _S_QIDX, _S_KIDX, _S_Q, _S_K, _S_V = 1, 2, 3, 4, 5, 6, 7
-_S_PKIDX, _S_PK, _S_PV, _S_TIER = 8, 9, 10, 11
+_S_PKIDX, _S_PK, _S_PV, _S_TIER, _S_WIDX = 8, 9, 10, 11, 12
 
 
 @dataclasses.dataclass(frozen=True)
@@ -102,6 +108,8 @@ WORKLOADS = {
                  fixed_lens=(32768,) * 64, reserve=32768),
         Workload("prefix_b128_16k", 4, 128, 64, 8576, 32, 8, 128, 128, False, 64, 1, 8, 1024, 1.0, 1.0,
                  len_range=(1024, 4096), prefix_len=16384, reserve=16384 + 4096),
+        Workload("mla_b64_32k_ih64", 6, 64, 64, 32832, 64, 1, 576, 512, True, 128, 64, 4, 2048, 0.5, 1.0,
+                 fixed_lens=(32768,) * 64, reserve=32768),
         Workload("tiered_b256_64k", 5, 256, 64, 524288, 16, 2, 128, 128, False, 0, 0, 0, 2048, 1.0, 1.0,
                  fixed_lens=(65536,) * 256, num_layers=8, reserve=65536, cache_fraction=0.25),
     ]
@@ -158,9 +166,28 @@ def index_queries(w: Workload, seed: int = 0) -> np.ndarray:
     return f32_to_bf16_bits(v.astype(np.float32))
 
 
-def index_weights(w: Workload) -> np.ndarray:
-    """Per-head indexer weights, fp32 [index_heads] (all ones: one head, weight 1)."""
-    return np.ones(w.index_heads, dtype=np.float32)
+def _weights(g: np.random.Generator, heads: int) -> np.ndarray:
+    if heads == 1:
+        return np.ones(1, dtype=np.float32)
+    return g.integers(-2, 4, size=heads).astype(np.float32)
+
+
+def index_weights(w: Workload, seed: int = 0) -> np.ndarray:
+    """Per-head indexer weights, fp32 [index_heads]: 1 for a single head, else integers
+    uniform in [-2, 3] (signed, so a ReLU taken after the weighting would show)."""
+    return _weights(_rng(seed, w, _S_WIDX), w.index_heads)
+
+
+def index_inputs(w: Workload, seed: int, heads: int, batch: Optional[int] = None):
+    """Indexer queries and weights for ``heads`` indexer heads instead of the workload's own
+    (head-count tests): bf16 bits [batch, heads, index_dim] and fp32 [heads]."""
+    batch = w.batch if batch is None else int(batch)
+    if heads == w.index_heads and batch <= w.batch:
+        return index_queries(w, seed)[:batch], index_weights(w, seed)
+    r = w.index_range
+    g = _rng(seed, w, _S_QIDX, heads, batch)
+    q = f32_to_bf16_bits(g.integers(-r, r + 1, size=(batch, heads, w.index_dim)).astype(np.float32))
+    return q, _weights(_rng(seed, w, _S_WIDX, heads), heads)
 
 
 def queries(w: Workload, seed: int = 0) -> np.ndarray:

@@ -157,15 +157,56 @@ def test_edge_lengths_and_page_sizes(tsa, P):
         _check_request(st, b, sc)
 
 
-def test_multihead_indexer(tsa):
-    st = staged("gqa_b32_8k", batch=4, index_heads=4)
-    assert st.params.index_heads == 4
-    sc = _scores_gpu(tsa, st)
-    for b in range(4):
+def _check_scores(st, sc, reqs):
+    for b in reqs:
         L = int(st.lens[b])
-        kidx, _, _ = synth.request_tokens(st.w, 0, b, L)
+        kidx, _, _ = synth.request_tokens(st.w, st.seed, b, L)
         ref = indexer.scores_bf16(st.qidx_np[b], st.widx_np, kidx)
-        assert np.array_equal(sc[b, :L].cpu().numpy().astype(np.float64), ref.astype(np.float64))
+        got = sc[b, :L].cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, ref.astype(np.float64)), f"scores differ, request {b}"
+
+
+@pytest.mark.parametrize("heads", [2, 4, 16, 17, 33, 64])
+def test_multihead_indexer(tsa, heads):
+    """Indexer heads on the matrix cores (2..64, padded to blocks of 16): bit-exact scores."""
+    st = staged("gqa_b32_8k", batch=4, index_heads=heads)
+    assert st.params.index_heads == heads
+    _check_scores(st, _scores_gpu(tsa, st), range(4))
+
+
+@pytest.mark.parametrize("P,name,heads", [(48, "gqa_b32_8k", 40), (16, "tiny_b5", 64), (8, "tiny_b5", 8)])
+def test_multihead_indexer_page_sizes(tsa, P, name, heads):
+    """Unaligned pages (48, index_dim 64), the smallest page the streaming kernel takes (16,
+    index_dim 32), and pages below it (8), where the register kernel holds up to 8 heads."""
+    lens = np.array([1, 47, 48, 49, 200, 777], dtype=np.int32)
+    st = staged(name, lens=lens, page_size=P, index_heads=heads)
+    _check_scores(st, _scores_gpu(tsa, st), range(len(lens)))
+
+
+def test_multihead_indexer_rejects_too_many_heads(tsa):
+    st = staged("tiny_b5", lens=np.array([30, 40], dtype=np.int32), page_size=8, index_heads=8)
+    p = tsa.decode_params(2, st.params.num_q_heads, st.params.top_k, st.params.max_len,
+                          st.params.sm_scale, index_heads=9)
+    sc = torch.empty((2, 64), dtype=torch.float32, device="cuda")
+    qidx = torch.zeros((2, 9, st.w.index_dim), dtype=torch.int16, device="cuda")
+    widx = torch.ones(9, dtype=torch.float32, device="cuda")
+    with pytest.raises(tsa.TsaError, match="index_heads"):
+        tsa.indexer_scores(st.pool, 0, p, qidx, widx, st.table_dev, st.lens_dev, sc)
+    p65 = tsa.decode_params(2, st.params.num_q_heads, st.params.top_k, st.params.max_len,
+                            st.params.sm_scale, index_heads=65)
+    st16 = staged("gqa_b32_8k", batch=2, index_heads=64)
+    with pytest.raises(tsa.TsaError, match="index_heads"):
+        tsa.indexer_scores(st16.pool, 0, p65, st16.qidx, st16.widx, st16.table_dev, st16.lens_dev, sc)
+
+
+def test_multihead_step_matches_oracle(tsa):
+    """The whole step with a 64-head indexer: scores, top-k sets and attention."""
+    st = staged("gqa_b32_8k", batch=6, index_heads=64)
+    sc = _scores_gpu(tsa, st)
+    st.step()
+    torch.cuda.synchronize()
+    for b in range(6):
+        _check_request(st, b, sc)
 
 
 def test_topk_kernel_ties_and_lengths(tsa):
@@ -255,6 +296,21 @@ def test_mla_full_size_sampled(tsa):
     tk = st.topk.cpu().numpy()
     assert (np.diff(tk, axis=1) > 0).all() and tk.min() >= 0 and tk.max() < 32768
     assert torch.isfinite(st.out).all()
+
+
+def test_mla_ih64_full_size_sampled(tsa):
+    """The 64 x 32k latent workload with a 64-head indexer on the matrix cores, in the launch
+    configuration the benchmark uses for it: sampled requests checked whole (scores bit-exact,
+    top-k sets, attention), every request checked for valid ascending selections."""
+    st = staged("mla_b64_32k_ih64")
+    assert st.params.index_heads == 64
+    sc = _scores_gpu(tsa, st)
+    st.step()
+    torch.cuda.synchronize()
+    errs = [_check_request(st, b, sc) for b in [0, 37, 63]]
+    print(f"mla_b64_32k_ih64: max normwise attention error {max(errs):.3e}")
+    tk = st.topk.cpu().numpy()
+    assert (np.diff(tk, axis=1) > 0).all() and tk.min() >= 0 and tk.max() < 32768
 
 
 def test_mla_large_logits_take_the_rescan_path(tsa):

@@ -61,6 +61,22 @@ def test_scores_exact_at_workload_extremes():
     assert s.tolist() == [D * r * r, 0, D * r * r] and D * r * r < 2 ** 24
 
 
+def test_scores_exact_at_multihead_extremes():
+    """The 64-head workload: every head at the largest logit and the largest weight, and the
+    signed case where the negative-weight heads alone fire.  The magnitude stays below 2^24, so
+    an fp32 accumulation of these integers is exact in any order."""
+    w = synth.get("mla_b64_32k_ih64")
+    H, D, r = w.index_heads, w.index_dim, w.index_range
+    q = np.full((H, D), r)
+    q[1::2] = -r                                         # odd heads see the negated key
+    wt = np.where(np.arange(H) % 2 == 0, 3, -2)
+    keys = np.stack([np.full(D, r), np.full(D, -r)])
+    s = indexer.scores(q, wt, keys)
+    top = D * r * r
+    assert s.tolist() == [3 * (H // 2) * top, -2 * (H // 2) * top]
+    assert 3 * H * top < 2 ** 24
+
+
 def test_bf16_decode_of_small_integers():
     """bf16 bit patterns of the integer range the workloads draw decode to those integers."""
     from oracle.bf16 import to_f64

@@ -56,3 +56,16 @@ def test_tier_positions_are_distinct_sorted():
     assert pos.min() >= 0 and pos.max() < 65536
     pos2, _ = synth.tier_positions(w, 0, 1, 0, 0, centres)
     assert not np.array_equal(pos, pos2)
+
+
+def test_multihead_indexer_inputs():
+    w = synth.get("mla_b64_32k_ih64")
+    q, wt = synth.index_queries(w), synth.index_weights(w)
+    assert q.shape == (64, 64, 128) and wt.shape == (64,)
+    assert set(np.unique(wt).tolist()) <= set(range(-2, 4))
+    assert (wt < 0).any() and (wt > 0).any()            # signed weights
+    q2, w2 = synth.index_inputs(w, 0, 64, 8)            # the workload's own heads: a slice
+    assert np.array_equal(q2, q[:8]) and np.array_equal(w2, wt)
+    q3, w3 = synth.index_inputs(synth.get("gqa_b32_8k"), 0, 17, 40)
+    assert q3.shape == (40, 17, 64) and w3.shape == (17,)
+    assert np.array_equal(synth.index_weights(synth.get("gqa_b32_8k")), [1.0])

@@ -30,7 +30,6 @@ WsLayout layout(const tsa_kv_pool& pool, const tsa_decode_params& p, bool with_a
     return w;
 }
 
-bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 tsa_status check_common(const tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
                         const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens) {
@@ -52,8 +51,8 @@ tsa_status check_indexer(const tsa_kv_pool* pool, const tsa_decode_params* p, co
                          const float* widx) {
     const int D = pool->d.index_dim;
     if (!D || !pool->idx) return fail(TSA_ERR_INVALID, "pool has no indexer keys");
-    if (!is_pow2(D / 8) || D / 8 > 64) return fail(TSA_ERR_UNSUPPORTED, "index_dim must be 8 x a power of two, <= 512");
-    if (p->index_heads < 1 || p->index_heads > 8) return fail(TSA_ERR_UNSUPPORTED, "index_heads must be in 1..8");
+    std::string why;
+    if (!tsa::indexer_supported(*pool, *p, &why)) return fail(TSA_ERR_UNSUPPORTED, why);
     if (p->batch > 0 && (!qidx || !widx)) return fail(TSA_ERR_INVALID, "NULL indexer query or weights");
     return TSA_OK;
 }

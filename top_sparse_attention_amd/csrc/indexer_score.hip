@@ -10,12 +10,15 @@
 //
 // A token's indexer key is index_dim bf16 values, stored contiguously, so a page of the indexer
 // cache is one contiguous run of page_size rows.  Two kernels:
-//  * single-head scores with pages of at least 16 tokens (every workload here): each wave owns
-//    a contiguous run of a request's tokens and streams it, 16 rows at a time, through a private
-//    ring of LDS slots with global-to-LDS loads (described where it is defined below);
-//  * any number of heads or smaller pages: LPT = index_dim / 8 lanes hold one token in
-//    registers (16-byte vectors, 8 values each), so one wave-wide load covers 64 / LPT whole
-//    tokens, and each head's dot product is reduced across those LPT lanes.
+//  * pages of at least 16 tokens and index_dim 32..256 (every workload here): each wave owns a
+//    contiguous run of a request's tokens and streams it, 16 rows at a time, through a private
+//    ring of LDS slots with global-to-LDS loads (described where it is defined below).  One
+//    head is dotted on the vector ALUs; 2..64 heads make the slot a [heads x dim] . [dim x 16]
+//    contraction, which runs on the matrix cores (H FLOP per byte read: at 64 heads the vector
+//    ALUs could not keep up with the stream);
+//  * smaller pages, up to 8 heads: LPT = index_dim / 8 lanes hold one token in registers
+//    (16-byte vectors, 8 values each), so one wave-wide load covers 64 / LPT whole tokens, and
+//    each head's dot product is reduced across those LPT lanes.
 // Positions whose page-table entry is not a valid page score -inf.
 #include "tsa_internal.h"
 
@@ -174,11 +177,24 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
 // ALIGNED: page_size is a power of two and a multiple of the 16-token slot, so every slot lies in
 // one page and the page id is the same for the whole wave.
-template <int D, bool ALIGNED>
+//
+// NB = 0: one head, dotted on the vector ALUs (v_dot2 on bf16 pairs).
+// NB > 0: H <= 16 NB heads on the matrix cores.  The heads are the rows and the slot's 16 tokens
+// the columns of S = Q K^T, one 16 x 16 x 32 MFMA per (16-head block, 32 dims).  The contraction
+// index is free to be relabelled, so MFMA k = 8 g + i of step c stands for dim g * D/4 + 8 c + i:
+// lane group g (lanes 16 g .. 16 g + 15) then reads the same quarter of its token's row as in the
+// one-head case, and the query registers follow the same relabelling.  The MFMA leaves heads
+// 4 g .. 4 g + 3 of every block with lane group g, so each lane applies ReLU and the weights to
+// its heads and the four groups are summed across lanes.  Heads H .. 16 NB - 1 are zero rows
+// with weight 0 and add exactly 0.
+template <int D, bool ALIGNED, int NB>
 __global__ void __launch_bounds__(256) indexer_score_lds_kernel(
-    const uint16_t* __restrict__ qidx, const float* __restrict__ widx,
+    const uint16_t* __restrict__ qidx, const float* __restrict__ widx, int H,
     const int32_t* __restrict__ page_table, int max_pages, int page_size, int page_shift,
     int num_pages, const int32_t* __restrict__ seq_lens, int max_len,
     const uint16_t* __restrict__ kpool, float* __restrict__ scores, int ld, int tok_per_wave) {
@@ -204,17 +220,35 @@ __global__ void __launch_bounds__(256) indexer_score_lds_kernel(
         wp[i] = (pid >= 0 && pid < num_pages) ? pid : -1;
     }
 
-    // query quarter g16 of this lane, as bf16 pairs
-    uint32_t q[G::kPart / 2];
-    {
+    // NB = 0: query quarter g16 of this lane, as bf16 pairs
+    uint32_t q[NB == 0 ? G::kPart / 2 : 1];
+    float w = 0.f;
+    // NB > 0: rows of head j16 of every block (the MFMA A operand), and the weights of the
+    // heads this lane's accumulator rows hold
+    uint4 qm[NB > 0 ? NB : 1][G::kPartChunks];
+    float wm[NB > 0 ? NB : 1][4];
+    if constexpr (NB == 0) {
         const uint4* src = reinterpret_cast<const uint4*>(qidx + int64_t(b) * D + g16 * G::kPart);
 #pragma unroll
         for (int c = 0; c < G::kPartChunks; ++c) {
             const uint4 v = src[c];
             q[4 * c + 0] = v.x; q[4 * c + 1] = v.y; q[4 * c + 2] = v.z; q[4 * c + 3] = v.w;
         }
+        w = widx[0];
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int h = nb * 16 + j16;
+            const uint4* src = reinterpret_cast<const uint4*>(qidx + (int64_t(b) * H + h) * D + g16 * G::kPart);
+#pragma unroll
+            for (int c = 0; c < G::kPartChunks; ++c) qm[nb][c] = h < H ? src[c] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int hw = nb * 16 + 4 * g16 + r;
+                wm[nb][r] = hw < H ? widx[hw] : 0.f;
+            }
+        }
     }
-    const float w = widx[0];
     wait_vm<0>();
 
     const uint32_t ring_base = uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)(&ring[wave][0][0])));
@@ -273,25 +307,48 @@ __global__ void __launch_bounds__(256) indexer_score_lds_kernel(
             wait_vm<0>();
         }
         const unsigned char* slot = &ring[wave][u % kRing][0];
-        float d = 0.f;
+        float sc;
+        if constexpr (NB == 0) {
+            float d = 0.f;
 #pragma unroll
-        for (int c = 0; c < G::kPartChunks; ++c) {
-            const uint4 v = *reinterpret_cast<const uint4*>(slot + rd_off[c]);
-            d = dot2(q[4 * c + 0], v.x, d);
-            d = dot2(q[4 * c + 1], v.y, d);
-            d = dot2(q[4 * c + 2], v.z, d);
-            d = dot2(q[4 * c + 3], v.w, d);
+            for (int c = 0; c < G::kPartChunks; ++c) {
+                const uint4 v = *reinterpret_cast<const uint4*>(slot + rd_off[c]);
+                d = dot2(q[4 * c + 0], v.x, d);
+                d = dot2(q[4 * c + 1], v.y, d);
+                d = dot2(q[4 * c + 2], v.z, d);
+                d = dot2(q[4 * c + 3], v.w, d);
+            }
+            d = sum4groups(d);
+            sc = w * fmaxf(d, 0.f);
+        } else {
+            f32x4 acc[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < G::kPartChunks; ++c) {
+                const bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(slot + rd_off[c]));
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qm[nb][c]),
+                                                                      kb, acc[nb], 0, 0, 0);
+            }
+            float part = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) part = fmaf(wm[nb][r], fmaxf(acc[nb][r], 0.f), part);
+            }
+            sc = sum4groups(part);
         }
-        d = sum4groups(d);
         const int t = t0 + u * kUnit + j16;
         if (g16 == 0 && t < t1) {
             const int page = ALIGNED ? wp[(t >> page_shift) - pg0] : wp[t / page_size - pg0];
-            scores[int64_t(b) * ld + t] = page >= 0 ? w * fmaxf(d, 0.f) : -INFINITY;
+            scores[int64_t(b) * ld + t] = page >= 0 ? sc : -INFINITY;
         }
     }
 }
 
-template <int D>
+template <int D, int NB>
 hipError_t launch_lds(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                       const void* qidx, const float* widx, const int32_t* page_table,
                       int max_pages, const int32_t* seq_lens, float* scores, int ld,
@@ -306,14 +363,27 @@ hipError_t launch_lds(const tsa_kv_pool& pool, int layer, const tsa_decode_param
     const uint16_t* kpool = static_cast<const uint16_t*>(pool.idx) + int64_t(layer) * pool.slots() * D;
     const bool aligned = shift >= 0 && d.page_size % kUnit == 0;
     if (aligned)
-        hipLaunchKernelGGL((indexer_score_lds_kernel<D, true>), grid, dim3(256), 0, s,
-                           static_cast<const uint16_t*>(qidx), widx, page_table, max_pages, d.page_size,
-                           shift, d.num_pages, seq_lens, p.max_len, kpool, scores, ld, tpw);
+        hipLaunchKernelGGL((indexer_score_lds_kernel<D, true, NB>), grid, dim3(256), 0, s,
+                           static_cast<const uint16_t*>(qidx), widx, p.index_heads, page_table, max_pages,
+                           d.page_size, shift, d.num_pages, seq_lens, p.max_len, kpool, scores, ld, tpw);
     else
-        hipLaunchKernelGGL((indexer_score_lds_kernel<D, false>), grid, dim3(256), 0, s,
-                           static_cast<const uint16_t*>(qidx), widx, page_table, max_pages, d.page_size,
-                           shift, d.num_pages, seq_lens, p.max_len, kpool, scores, ld, tpw);
+        hipLaunchKernelGGL((indexer_score_lds_kernel<D, false, NB>), grid, dim3(256), 0, s,
+                           static_cast<const uint16_t*>(qidx), widx, p.index_heads, page_table, max_pages,
+                           d.page_size, shift, d.num_pages, seq_lens, p.max_len, kpool, scores, ld, tpw);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_lds_heads(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
+                            const void* qidx, const float* widx, const int32_t* page_table,
+                            int max_pages, const int32_t* seq_lens, float* scores, int ld,
+                            hipStream_t s, int shift) {
+    const int h = p.index_heads;
+    if (h == 1) return launch_lds<D, 0>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
+    if (h <= 16) return launch_lds<D, 1>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
+    if (h <= 32) return launch_lds<D, 2>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
+    if (h <= tsa::kMaxIndexHeads) return launch_lds<D, 4>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
+    return hipErrorInvalidValue;
 }
 
 template <int LPT>
@@ -348,24 +418,45 @@ hipError_t launch_lpt(const tsa_kv_pool& pool, int layer, const tsa_decode_param
 
 namespace tsa {
 
+static bool lds_kernel_takes(const tsa_kv_pool& pool) {
+    const int D = pool.d.index_dim;
+    return pool.d.page_size >= kMinPage && (D == 32 || D == 64 || D == 128 || D == 256);
+}
+
+bool indexer_supported(const tsa_kv_pool& pool, const tsa_decode_params& p, std::string* why) {
+    const int D = pool.d.index_dim;
+    if (D < 8 || D % 8 || (D / 8 & (D / 8 - 1)) || D / 8 > 64) {
+        *why = "index_dim must be 8 x a power of two, <= 512";
+        return false;
+    }
+    const int hmax = lds_kernel_takes(pool) ? kMaxIndexHeads : 8;
+    if (p.index_heads < 1 || p.index_heads > hmax) {
+        *why = "index_heads must be in 1.." + std::to_string(hmax) +
+               (hmax == 8 ? " (more heads need index_dim 32..256 and pages of >= 16 tokens)" : "");
+        return false;
+    }
+    return true;
+}
+
 hipError_t launch_indexer_scores(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                                  const void* qidx, const float* widx, const int32_t* page_table,
                                  int max_pages, const int32_t* seq_lens, float* scores, int ld,
                                  hipStream_t s) {
-    if (p.index_heads == 1 && pool.d.page_size >= kMinPage) {
+    if (lds_kernel_takes(pool)) {
         int shift = -1;
         if ((pool.d.page_size & (pool.d.page_size - 1)) == 0) {
             shift = 0;
             while ((1 << shift) < pool.d.page_size) ++shift;
         }
         switch (pool.d.index_dim) {
-            case 32: return launch_lds<32>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
-            case 64: return launch_lds<64>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
-            case 128: return launch_lds<128>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
-            case 256: return launch_lds<256>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
+            case 32: return launch_lds_heads<32>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
+            case 64: return launch_lds_heads<64>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
+            case 128: return launch_lds_heads<128>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
+            case 256: return launch_lds_heads<256>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
             default: break;
         }
     }
+    if (p.index_heads > 8) return hipErrorInvalidValue;   // the register kernel holds at most 8 heads
     switch (pool.d.index_dim / 8) {
         case 1: return launch_lpt<1>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s);
         case 2: return launch_lpt<2>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s);

@@ -53,6 +53,9 @@ hipError_t launch_kv_append(const tsa_kv_pool& pool, int layer, int n_tok, const
                             const void* idx_src, int32_t* bad, hipStream_t s);
 
 // Indexer score of every cached token (fp32 [B][ld]).
+constexpr int kMaxIndexHeads = 64;
+// Whether the indexer kernels take this pool / head count (reason in *why when not).
+bool indexer_supported(const tsa_kv_pool& pool, const tsa_decode_params& p, std::string* why);
 hipError_t launch_indexer_scores(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                                  const void* qidx, const float* widx, const int32_t* page_table,
                                  int max_pages, const int32_t* seq_lens, float* scores, int ld,

@@ -84,14 +84,7 @@ def stage(w, seed: int = 0, batch: Optional[int] = None, lens: Optional[np.ndarr
         table, num, saved = pool.build_tables(lens, max_pages)
     H_I = w.index_heads if index_heads is None else int(index_heads)
 
-    qidx_np = synth.index_queries(w, seed)[:B]
-    if H_I != w.index_heads:
-        rng = np.random.default_rng([seed, 77])
-        r = w.index_range
-        qidx_np = synth.f32_to_bf16_bits(rng.integers(-r, r + 1, size=(B, H_I, w.index_dim)).astype(np.float32))
-        widx_np = rng.integers(-2, 4, size=H_I).astype(np.float32)
-    else:
-        widx_np = synth.index_weights(w)
+    qidx_np, widx_np = synth.index_inputs(w, seed, H_I, B)
     q_np = synth.queries(w, seed)[:B]
 
     table_dev = _dev(table, device)

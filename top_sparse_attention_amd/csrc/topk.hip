@@ -13,10 +13,11 @@
 // histogram and the key-range slots are double-buffered by pass parity (the next pass's copy
 // is cleared during the current one), and the wave-level scans and min / max use DPP lane
 // moves rather than LDS round trips.  After the passes, every element whose key exceeds the threshold is
-// kept, and of the elements equal to it the lowest positions fill the rest; one block-wide
-// scan over positions (each thread owns a contiguous run) of the packed counts (above,
-// equal) yields both the tie ranks and the output offsets, so the output comes out ascending
-// with no sort.
+// kept, and of the elements equal to it the lowest positions fill the rest; a prefix count in
+// position order of the packed counts (above, equal) yields both the tie ranks and the output
+// offsets, so the output comes out ascending with no sort.  Each wave owns a contiguous block of
+// positions and reads it with wave-contiguous 16-byte loads (one 1 KiB run per instruction);
+// the prefix is then a wave scan per load group plus one block scan of the wave totals.
 #include "tsa_internal.h"
 
 namespace {
@@ -112,28 +113,42 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
         return;
     }
     const float* s = scores + int64_t(b) * ld;
-    const int base = tid * IPT;
+    // Wave w owns the contiguous positions [w * 64 * IPT, (w + 1) * 64 * IPT).  Inside it, element
+    // (g, e) of lane l (g < G groups of E values) sits at 64 E g + E l + e: every load instruction
+    // of the wave then covers one contiguous run of 64 E values (1 KiB when E = 4), and position
+    // order within the wave is (g, lane, e).
+    constexpr int E = IPT < 4 ? IPT : 4;
+    constexpr int G = IPT / E;
+    const int lane = tid & 63;
+    const int wbase = (tid >> 6) * 64 * IPT + E * lane;   // position of element (0, 0)
     uint32_t key[IPT];
-    if (IPT >= 4 && (ld & 3) == 0) {
+    if (E == 4 && (ld & 3) == 0) {
 #pragma unroll
-        for (int i = 0; i < IPT; i += 4) {
+        for (int g = 0; g < G; ++g) {
+            const int p0 = wbase + 64 * E * g;
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (base + i + 3 < len) {
-                v = *reinterpret_cast<const float4*>(s + base + i);
+            if (p0 + 3 < len) {
+                v = *reinterpret_cast<const float4*>(s + p0);
             } else {
-                if (base + i < len) v.x = s[base + i];
-                if (base + i + 1 < len) v.y = s[base + i + 1];
-                if (base + i + 2 < len) v.z = s[base + i + 2];
+                if (p0 < len) v.x = s[p0];
+                if (p0 + 1 < len) v.y = s[p0 + 1];
+                if (p0 + 2 < len) v.z = s[p0 + 2];
             }
-            key[i] = order_key(v.x);
-            key[i + 1] = order_key(v.y);
-            key[i + 2] = order_key(v.z);
-            key[i + 3] = order_key(v.w);
+            key[4 * g + 0] = order_key(v.x);
+            key[4 * g + 1] = order_key(v.y);
+            key[4 * g + 2] = order_key(v.z);
+            key[4 * g + 3] = order_key(v.w);
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < IPT; ++i) key[i] = (base + i < len) ? order_key(s[base + i]) : 0u;
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int p = wbase + 64 * E * g + e;
+                key[E * g + e] = p < len ? order_key(s[p]) : 0u;
+            }
     }
+    auto valid = [&](int i) { return wbase + 64 * E * (i / E) + (i % E) < len; };
 
     uint32_t prefix = 0, mask = 0;
     int remaining = k;  // how many of the elements matching `prefix` under `mask` to keep
@@ -152,7 +167,7 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
         uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
         for (int i = 0; i < IPT; ++i) {
-            if (base + i < len && (key[i] & mask) == prefix) {
+            if (valid(i) && (key[i] & mask) == prefix) {
                 atomicAdd(&h[((key[i] >> shift) & 255u) * kCopies + copy], 1u);
                 kmin = min(kmin, key[i]);
                 kmax = max(kmax, key[i]);
@@ -200,31 +215,51 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
         if (in_bin == remaining) break;  // the whole bin is kept: no finer digit matters
     }
 
-    // final selection: above the threshold, or equal to it and among the first `remaining`;
-    // one scan of the packed counts (above << 16 | equal): an exclusive prefix of either count
-    // stays below 2^16 (at most 64 * kThreads elements, fewer than k above the threshold), so
-    // the low field never carries into the high one
-    int gt = 0, eq = 0;
+    // final selection: above the threshold, or equal to it and among the first `remaining` in
+    // position order.  Counts are packed (above << 16 | equal): an exclusive prefix of either
+    // count stays below 2^16 (at most 64 * kThreads elements, fewer than k above the threshold),
+    // so the low field never carries into the high one.  The prefix of an element in position
+    // order is: earlier waves (one block scan of the wave totals), then earlier groups of its
+    // wave (their wave totals), then earlier lanes of its group (a wave scan per group).
+    uint32_t cnt[G], pre[G];
+    uint32_t run = 0;
 #pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-        const bool v = base + i < len;
-        const uint32_t m = key[i] & mask;
-        gt += (v && m > prefix);
-        eq += (v && m == prefix);
+    for (int g = 0; g < G; ++g) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = E * g + e;
+            const bool v = valid(i);
+            const uint32_t m = key[i] & mask;
+            c += (v && m > prefix) ? 0x10000u : 0u;
+            c += (v && m == prefix) ? 1u : 0u;
+        }
+        cnt[g] = c;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const uint32_t x = wave_inclusive_sum(cnt[g]);
+        pre[g] = run + x - cnt[g];
+        run += uint32_t(__builtin_amdgcn_readlane(int(x), 63));
     }
     int total;
-    const uint32_t packed = uint32_t(block_exclusive_scan(int((uint32_t(gt) << 16) | uint32_t(eq)), sh_scan[pass & 1], &total));
-    const int gt_before = int(packed >> 16), eq_before = int(packed & 0xffffu);
-    // output offset: every earlier element above, plus the earlier equal ones that are kept
-    int off = gt_before + min(eq_before, remaining);
-    int eq_rank = eq_before;
+    const uint32_t wave_pre = uint32_t(block_exclusive_scan(lane == 63 ? int(run) : 0, sh_scan[pass & 1], &total));
 #pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-        const bool v = base + i < len;
-        const uint32_t m = key[i] & mask;
-        bool take = v && m > prefix;
-        if (v && m == prefix) take = eq_rank++ < remaining;
-        if (take && off < k) o[off++] = base + i;
+    for (int g = 0; g < G; ++g) {
+        const uint32_t packed = wave_pre + pre[g];
+        const int gt_before = int(packed >> 16), eq_before = int(packed & 0xffffu);
+        // output offset: every earlier element above, plus the earlier equal ones that are kept
+        int off = gt_before + min(eq_before, remaining);
+        int eq_rank = eq_before;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = E * g + e;
+            const bool v = valid(i);
+            const uint32_t m = key[i] & mask;
+            bool take = v && m > prefix;
+            if (v && m == prefix) take = eq_rank++ < remaining;
+            if (take && off < k) o[off++] = wbase + 64 * E * g + e;
+        }
     }
 }
 

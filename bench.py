@@ -324,6 +324,8 @@ def main():
                     help="requests of the tiered workload (the full 256 needs 128 GiB of pinned memory)")
     ap.add_argument("--tier-unit", choices=("page", "token"), default="page",
                     help="cache unit of the tiered workload: whole pages or single token rows")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step as one replay of a captured graph (tsa_step_graph_*)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="first run a plain streaming copy of this many MiB (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -380,15 +382,22 @@ def main():
         if ev is not None:
             ev[4].record(stream)
 
+    timed = step
+    if args.graph:
+        graph = tsa.StepGraph(st.pool, 0, st.params, st.q, st.qidx, st.widx, st.table_dev, st.lens_dev,
+                              st.out, st.workspace, topk_out=st.topk,
+                              append=None if st.new_req is None else
+                              (st.new_req, st.new_pos, st.new_k, st.new_v, st.new_idx, None))
+        timed = lambda: graph.launch(stream)
     for _ in range(args.warmup):
-        step()
+        timed()
     torch.cuda.synchronize()
     # The throughput pass has no event between kernels: on this runtime each such event adds
     # a few microseconds of idle time before the next kernel (about 18 us over the 4 inner
     # events of a step, measured), which would charge the step for its own instrumentation.
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        timed()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
@@ -443,7 +452,8 @@ def main():
         "config": {"workload": w.name, "requests": B, "context": int(lens.max()),
                    "top_k": w.top_k, "page_size": w.page_size, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim_k": w.head_dim_k, "head_dim_v": w.head_dim_v,
-                   "index_dim": D_I, "index_heads": w.index_heads, "parallelism": "none"},
+                   "index_dim": D_I, "index_heads": w.index_heads, "parallelism": "none",
+                   "launch": "graph" if args.graph else "eager"},
         "kernels_ms": {"kv_append": round(t_append, 5), "indexer_score": round(t_index, 5),
                        "topk": round(t_topk, 5), "attention": round(t_attn, 5)},
         "kernel_timing": "HIP events between kernels on the launch stream, over a second pass of "

@@ -221,6 +221,43 @@ tsa_status tsa_sparse_decode_attn(tsa_kv_pool* pool, int32_t layer, const tsa_de
                                   void* workspace, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * Captured step.  GLM5.3 page, paragraph on serving-engine prefill and decode (the GLM-5.2
+ * studies): running the decode step on a fixed graph-execution path lowered the time per output
+ * token; TileRT paragraph: launch overhead is worth removing.  Here the step's launches are
+ * recorded once and replayed by one launch.  The
+ * step (an optional kv_append, then tsa_sparse_decode_attn) is recorded into a HIP graph over
+ * fixed device pointers; each tsa_step_graph_launch replays it on the given stream, reading
+ * whatever those buffers hold at that time (new queries, lengths, page tables of the same
+ * shape).  Sizes, the pool, the parameters and the pointers are fixed at creation; anything
+ * else needs a new graph.  The graph records kernel launches only (no memset or copy nodes).
+ * Replays that overlap on one workspace race, as eager calls would.  Errors: the same checks
+ * as the eager calls, at creation; TSA_ERR_HIP if capture or instantiation fails.
+ * ---------------------------------------------------------------------------------- */
+typedef struct tsa_append_args {
+    int32_t n_tok;            /* new tokens; 0 records no append */
+    const int32_t* req_dev;   /* [n_tok] request of each token */
+    const int32_t* pos_dev;   /* [n_tok] its position */
+    const void* k_src;        /* as tsa_kv_append */
+    const void* v_src;
+    const void* idx_src;
+    int32_t* bad_dev;         /* nullable rejected-token counter (accumulates over replays) */
+} tsa_append_args;
+
+typedef struct tsa_step_graph tsa_step_graph;
+
+/* Record the step.  append may be NULL.  The other arguments are those of
+ * tsa_sparse_decode_attn (the append uses the same page table, max_pages and batch). */
+tsa_status tsa_step_graph_create(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                                 const tsa_append_args* append, const void* q_dev,
+                                 const void* qidx_dev, const float* widx_dev,
+                                 const int32_t* page_table_dev, int32_t max_pages,
+                                 const int32_t* seq_lens_dev, float* out_dev, int32_t* topk_dev,
+                                 void* workspace, size_t ws_bytes, tsa_step_graph** graph);
+/* Replay on `stream` (NULL = the null stream). */
+tsa_status tsa_step_graph_launch(tsa_step_graph* graph, void* stream);
+tsa_status tsa_step_graph_destroy(tsa_step_graph* graph);
+
+/* ------------------------------------------------------------------------------------
  * Tiered KV: an HBM page cache with LRU eviction over a host-memory copy of every page.
  * [GLM5.3 page], HiSparse paragraph: the KV cache lives in host DRAM and the HBM part acts as
  * an LRU cache; a top-k selection that misses loads the page from DRAM, the least recently

@@ -187,6 +187,23 @@ def test_device_calls_refuse_metadata_pool():
     assert e.value.status == _lib.TSA_ERR_INVALID
 
 
+def test_step_graph_refuses_before_capture():
+    """Argument errors of the captured step are reported before anything touches the GPU."""
+    import ctypes as C
+    pool = _pool(10, 16, index_dim=32)
+    p = tsa.decode_params(1, 8, 4, 16, 0.125)
+    lib = _lib.load()
+    h = C.c_void_p()
+    st = lib.tsa_step_graph_create(pool.handle, 0, C.byref(p), None, None, None, None, None, 1, None,
+                                   None, None, None, 0, C.byref(h))
+    assert st == _lib.TSA_ERR_INVALID and b"device memory" in lib.tsa_last_error()
+    st = lib.tsa_step_graph_create(pool.handle, 0, C.byref(p), None, None, None, None, None, 1, None,
+                                   None, None, None, 0, None)
+    assert st == _lib.TSA_ERR_INVALID
+    assert lib.tsa_step_graph_launch(None, None) == _lib.TSA_ERR_INVALID
+    assert lib.tsa_step_graph_destroy(None) == _lib.TSA_OK
+
+
 class _FakeDev:
     """Stands in for a device tensor in argument-validation tests (never dereferenced)."""
     def __init__(self, max_pages):

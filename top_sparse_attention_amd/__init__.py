@@ -21,7 +21,7 @@ from ._lib import DecodeParams, PoolDesc, TsaError, call, load  # noqa: F401
 
 __all__ = ["KvPool", "DecodeParams", "TsaError", "load", "decode_params", "workspace_bytes",
            "indexer_scores", "topk", "indexer_topk", "sparse_attn_gather", "sparse_decode_attn",
-           "abi_version"]
+           "abi_version", "StepGraph"]
 
 
 def _i32p(a: Optional[np.ndarray]):
@@ -249,6 +249,42 @@ def sparse_attn_gather(pool, layer, p, q, topk_idx, table_dev, seq_lens, out, wo
     call("tsa_sparse_attn_gather", pool.handle, int(layer), C.byref(p), _ptr(q), _ptr(topk_idx),
          _ptr(table_dev), int(table_dev.shape[-1]), _ptr(seq_lens), _ptr(out), _ptr(workspace),
          _nbytes(workspace), _stream(stream))
+
+
+class StepGraph:
+    """The decode step (optional kv_append, then scores, top-k, attention) recorded once into a HIP
+    graph over these tensors; ``launch`` replays it (see tsa_step_graph_create).  The tensors
+    must stay alive and keep their shapes while the graph exists."""
+
+    def __init__(self, pool, layer, p, q, qidx, widx, table_dev, seq_lens, out, workspace,
+                 topk_out=None, append=None):
+        self._keep = [pool, p, q, qidx, widx, table_dev, seq_lens, out, workspace, topk_out]
+        ap = None
+        if append is not None:
+            req, pos, k_src, v_src, idx_src, bad = append
+            ap = _lib.AppendArgs(int(req.numel()), _ptr(req), _ptr(pos), _ptr(k_src), _ptr(v_src),
+                                 _ptr(idx_src), _ptr(bad))
+            self._keep += [ap, req, pos, k_src, v_src, idx_src, bad]
+        h = C.c_void_p()
+        call("tsa_step_graph_create", pool.handle, int(layer), C.byref(p),
+             None if ap is None else C.byref(ap), _ptr(q), _ptr(qidx), _ptr(widx), _ptr(table_dev),
+             int(table_dev.shape[-1]), _ptr(seq_lens), _ptr(out), _ptr(topk_out), _ptr(workspace),
+             _nbytes(workspace), C.byref(h))
+        self.handle = h
+
+    def launch(self, stream=None):
+        call("tsa_step_graph_launch", self.handle, _stream(stream))
+
+    def close(self):
+        if getattr(self, "handle", None):
+            call("tsa_step_graph_destroy", self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def sparse_decode_attn(pool, layer, p, q, qidx, widx, table_dev, seq_lens, out, workspace,

@@ -33,6 +33,11 @@ class DecodeParams(C.Structure):
                 ("max_len", i32), ("sm_scale", f32)]
 
 
+class AppendArgs(C.Structure):
+    _fields_ = [("n_tok", i32), ("req_dev", vp), ("pos_dev", vp), ("k_src", vp), ("v_src", vp),
+                ("idx_src", vp), ("bad_dev", vp)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "tsa_last_error": (C.c_char_p, []),
@@ -54,6 +59,10 @@ SIGNATURES = {
     "tsa_sparse_attn_gather": (i32, [vp, i32, C.POINTER(DecodeParams), vp, vp, vp, i32, vp, vp, vp, sz, vp]),
     "tsa_sparse_decode_attn": (i32, [vp, i32, C.POINTER(DecodeParams), vp, vp, vp, vp, i32, vp, vp, vp,
                                      vp, sz, vp]),
+    "tsa_step_graph_create": (i32, [vp, i32, C.POINTER(DecodeParams), C.POINTER(AppendArgs), vp, vp, vp,
+                                    vp, i32, vp, vp, vp, vp, sz, C.POINTER(vp)]),
+    "tsa_step_graph_launch": (i32, [vp, vp]),
+    "tsa_step_graph_destroy": (i32, [vp]),
     "tsa_lru_create": (i32, [vp, i32, i32, i32, vp, vp, C.POINTER(vp)]),
     "tsa_lru_destroy": (i32, [vp]),
     "tsa_lru_preload": (i32, [vp, i64, P_i64]),

@@ -196,3 +196,78 @@ tsa_status tsa_sparse_decode_attn(tsa_kv_pool* pool, int32_t layer, const tsa_de
 }
 
 }  // extern "C"
+
+// ---- captured step -------------------------------------------------------------------------
+// The step's launches are recorded on a private stream with the same entry points an eager
+// caller uses (same checks, same plan), so a replay runs exactly the eager kernels.
+struct tsa_step_graph {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+extern "C" {
+
+tsa_status tsa_step_graph_create(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                                 const tsa_append_args* append, const void* q_dev,
+                                 const void* qidx_dev, const float* widx_dev,
+                                 const int32_t* page_table_dev, int32_t max_pages,
+                                 const int32_t* seq_lens_dev, float* out_dev, int32_t* topk_dev,
+                                 void* workspace, size_t ws_bytes, tsa_step_graph** graph) {
+    if (!graph) return fail(TSA_ERR_INVALID, "graph is NULL");
+    *graph = nullptr;
+    if (!pool || !p) return fail(TSA_ERR_INVALID, "NULL argument");
+    if (!pool->k) return fail(TSA_ERR_INVALID, "pool has no device memory");
+    hipStream_t cs = nullptr;
+    tsa_status st = tsa::hip_check(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking), "hipStreamCreate");
+    if (st) return st;
+    st = tsa::hip_check(hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed), "hipStreamBeginCapture");
+    if (st) {
+        (void)hipStreamDestroy(cs);
+        return st;
+    }
+    if (append && append->n_tok > 0)
+        st = tsa_kv_append(pool, layer, append->n_tok, append->req_dev, append->pos_dev,
+                           page_table_dev, p->batch, max_pages, append->k_src, append->v_src,
+                           append->idx_src, append->bad_dev, cs);
+    if (st == TSA_OK)
+        st = tsa_sparse_decode_attn(pool, layer, p, q_dev, qidx_dev, widx_dev, page_table_dev,
+                                    max_pages, seq_lens_dev, out_dev, topk_dev, workspace, ws_bytes, cs);
+    const std::string why = st ? std::string(tsa_last_error()) : std::string();
+    hipGraph_t g = nullptr;
+    const hipError_t ec = hipStreamEndCapture(cs, &g);
+    (void)hipStreamDestroy(cs);
+    if (st) {
+        if (g) (void)hipGraphDestroy(g);
+        return fail(st, why);
+    }
+    if ((st = tsa::hip_check(ec, "hipStreamEndCapture"))) {
+        if (g) (void)hipGraphDestroy(g);
+        return st;
+    }
+    hipGraphExec_t exec = nullptr;
+    if ((st = tsa::hip_check(hipGraphInstantiate(&exec, g, nullptr, nullptr, 0), "hipGraphInstantiate"))) {
+        (void)hipGraphDestroy(g);
+        return st;
+    }
+    *graph = new tsa_step_graph{g, exec};
+    return TSA_OK;
+}
+
+tsa_status tsa_step_graph_launch(tsa_step_graph* graph, void* stream) {
+    if (!graph) return fail(TSA_ERR_INVALID, "graph is NULL");
+    return tsa::hip_check(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)), "hipGraphLaunch");
+}
+
+tsa_status tsa_step_graph_destroy(tsa_step_graph* graph) {
+    if (!graph) return TSA_OK;
+    tsa_status st = TSA_OK;
+    if (graph->exec) st = tsa::hip_check(hipGraphExecDestroy(graph->exec), "hipGraphExecDestroy");
+    if (graph->graph) {
+        const tsa_status s2 = tsa::hip_check(hipGraphDestroy(graph->graph), "hipGraphDestroy");
+        if (st == TSA_OK) st = s2;
+    }
+    delete graph;
+    return st;
+}
+
+}  // extern "C"

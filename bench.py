@@ -178,6 +178,74 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, mib: int):
     print(json.dumps(doc, indent=1, sort_keys=True))
 
 
+def bench_mla_modes(args):
+    """Latent attention in its two modes (GLM5.3 page, MLA-modes paragraph) at several context
+    lengths, on the same selected positions: the MQA mode (every one of the 64 heads reads one
+    576-dim latent row per token; matrix-core kernel) against the MHA mode (each head reads its own
+    192-dim key and 128-dim value; vector-ALU kernel with one query head per KV head).  Values
+    are random bf16 drawn on the device; the parity of both modes is the tests' business.
+    Prints one JSON line."""
+    import torch
+    import top_sparse_attention_amd as tsa
+    from top_sparse_attention_amd import KvPool, decode_params, workspace_bytes
+
+    tsa.load()
+    B, H, K, P = 64, 64, 2048, 64
+    scale = 1.0 / np.sqrt(192.0)
+    rng = np.random.default_rng(args.seed)
+    modes = {"mqa": dict(hkv=1, dk=576, dv=512, alias=True), "mha": dict(hkv=H, dk=192, dv=128, alias=False)}
+    points = []
+    for L in (256, 512, 1024, 2048, 4096, 8192):
+        n_sel = min(L, K)
+        pos = np.full((B, K), -1, dtype=np.int32)
+        for b in range(B):
+            pos[b, :n_sel] = np.sort(rng.choice(L, n_sel, replace=False))
+        topk = torch.from_numpy(pos).cuda()
+        lens = np.full(B, L, dtype=np.int32)
+        pt = {"L": L, "selected": n_sel}
+        for name, m in modes.items():
+            npages = B * (-(-L // P)) + B
+            pool = KvPool(npages, P, m["hkv"], m["dk"], m["dv"], v_from_k=m["alias"],
+                          free_order=rng.permutation(npages).astype(np.int32))
+            table, _, _ = pool.build_tables(lens, -(-L // P))
+            pool.k.normal_(0.0, 0.5)
+            if pool.v is not None:
+                pool.v.normal_(0.0, 0.5)
+            p = decode_params(B, H, K, L, scale)
+            q = torch.randn((B, H, m["dk"]), device="cuda").to(torch.bfloat16)
+            out = torch.empty((B, H, m["dv"]), dtype=torch.float32, device="cuda")
+            ws = torch.empty(max(workspace_bytes(pool, p), 256), dtype=torch.uint8, device="cuda")
+            tdev = torch.from_numpy(table).cuda()
+            ldev = torch.from_numpy(lens).cuda()
+            call = lambda: tsa.sparse_attn_gather(pool, 0, p, q, topk, tdev, ldev, out, ws)
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = 20
+            e0.record()
+            for _ in range(n):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / n
+            row = m["hkv"] * (m["dk"] * 2 + (0 if m["alias"] else m["dv"] * 2))
+            nbytes = B * n_sel * row + B * H * m["dk"] * 2 + B * H * m["dv"] * 4 + B * K * 4
+            flops = 2.0 * B * n_sel * H * (m["dk"] + m["dv"])
+            pt[f"{name}_us"] = round(us, 2)
+            pt[f"{name}_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+            pt[f"{name}_tflops"] = round(flops / (us * 1e-6) / 1e12, 1)
+            del pool, q, out, ws, tdev, ldev
+            torch.cuda.empty_cache()
+        points.append(pt)
+        print(f"[bench] L={L}: MQA {pt['mqa_us']} us, MHA {pt['mha_us']} us", file=sys.stderr, flush=True)
+    faster = [pt["L"] for pt in points if pt["mha_us"] < pt["mqa_us"]]
+    print(json.dumps({"metric": "MLA decode attention, MQA mode vs MHA mode (us per call, 64 requests, "
+                                "64 heads, top-2048)", "unit": "us", "higher_is_better": False,
+                      "dtype": "bf16", "data": "synthetic",
+                      "mha_faster_at": faster, "points": points}), flush=True)
+
+
 def bench_tier(args):
     """The tiered workload: per step, every layer plans its pages on the host, fetches the
     misses on a side stream and attends over the HBM cache; prints one JSON line with
@@ -324,6 +392,8 @@ def main():
                     help="requests of the tiered workload (the full 256 needs 128 GiB of pinned memory)")
     ap.add_argument("--tier-unit", choices=("page", "token"), default="page",
                     help="cache unit of the tiered workload: whole pages or single token rows")
+    ap.add_argument("--mla-modes", action="store_true",
+                    help="compare latent attention in MQA mode and MHA mode over context lengths and exit")
     ap.add_argument("--graph", action="store_true",
                     help="time the step as one replay of a captured graph (tsa_step_graph_*)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -348,6 +418,9 @@ def main():
     import top_sparse_attention_amd as tsa
     from top_sparse_attention_amd import workload
 
+    if args.mla_modes:
+        bench_mla_modes(args)
+        return
     if synth.get(args.workload).num_layers > 1:
         bench_tier(args)
         return

@@ -24,6 +24,8 @@ for checking by eye against them:
                thì đo được rõ", for the sequential-scan pathology).
 * ``roofline`` arithmetic intensity of MQA-mode MLA decode (GLM5.3 page, roofline
                paragraph; the equations themselves did not survive extraction).
+* ``mla``      the MHA and MQA modes of latent attention and their costs (GLM5.3
+               page, MLA-modes paragraph).
 
 Nothing here imports the HIP package, and the HIP package imports nothing here.
 Inputs come from ``synth`` (random draws only) or from literal arrays in tests.

@@ -35,6 +35,11 @@ Workloads (the shapes the pages discuss, with synthetic values):
                      query heads, one key head, a weighted sum of per-head ReLU
                      logits).  Scores stay exact in fp32: |score| <= 64 x 3 x
                      128 x 4 x 4 = 393,216 < 2^24.
+* ``mla_mha_b64_4k`` the MHA mode of the same latent attention (GLM5.3 page,
+                     MLA-modes paragraph): 64 requests x 4096 tokens, 64 query
+                     heads each with its own 192-dim key (128 projected + 64
+                     rotary) and 128-dim value, top-k 2048.  Keys and values
+                     are drawn directly (no trained up-projections).
 * ``tiered_b256_64k`` 256 requests x 65536 tokens x 8 layers; the HBM page
                      cache holds a quarter of the pages (GLM5.3 sparse-attention
                      page, HiSparse paragraph).  Positions come from a seeded
@@ -95,6 +100,7 @@ class Workload:
 #   tiny:   61 pages used + 5 spare                           = 66
 #   gqa:    32 x (8192/64) + 32                               = 4128
 #   mla:    64 x (32768/64) + 64                              = 32832
+#   mha:    64 x (4096/64) + 64                               = 4160
 #   prefix: 256 shared + 128 x (4096/64) private + 128        = 8576
 #   tiered: per layer 256 x (65536/64) = 262144 logical pages (host copy);
 #           the HBM cache is 25% of all layers' pages          = 524288 slots
@@ -110,6 +116,8 @@ WORKLOADS = {
                  len_range=(1024, 4096), prefix_len=16384, reserve=16384 + 4096),
         Workload("mla_b64_32k_ih64", 6, 64, 64, 32832, 64, 1, 576, 512, True, 128, 64, 4, 2048, 0.5, 1.0,
                  fixed_lens=(32768,) * 64, reserve=32768),
+        Workload("mla_mha_b64_4k", 7, 64, 64, 4160, 64, 64, 192, 128, False, 128, 1, 4, 2048, 0.5, 1.0,
+                 fixed_lens=(4096,) * 64, reserve=4096),
         Workload("tiered_b256_64k", 5, 256, 64, 524288, 16, 2, 128, 128, False, 0, 0, 0, 2048, 1.0, 1.0,
                  fixed_lens=(65536,) * 256, num_layers=8, reserve=65536, cache_fraction=0.25),
     ]

@@ -548,12 +548,14 @@ bool mfma_latent_applicable(const tsa_kv_pool& pool, const tsa_decode_params& p)
 }
 
 int mfma_latent_chunk(const tsa_decode_params& p, int* splits) {
-    const int tiles = int(ceil_div(p.top_k, kTile));
+    // no request selects more than min(top_k, max_len) tokens: split that, not top_k
+    const int k_eff = std::max(1, std::min(p.top_k, p.max_len));
+    const int tiles = int(ceil_div(k_eff, kTile));
     int s = int(ceil_div(256, std::max(p.batch, 1)));   // one workgroup per CU
     s = std::max(1, std::min({s, tiles, 64}));   // the combine takes at most 64 splits
     s = std::max(s, int(ceil_div(tiles, kMaxChunk / kTile)));   // the row list fits in LDS
     const int chunk = int(ceil_div(tiles, s)) * kTile;
-    *splits = int(ceil_div(p.top_k, chunk));
+    *splits = int(ceil_div(k_eff, chunk));
     return chunk;
 }
 

@@ -402,12 +402,13 @@ AttnPlan plan_attention(const tsa_kv_pool& pool, const tsa_decode_params& p) {
     const int G = p.num_q_heads / d.num_kv_heads;
     const int T = pick_tile(G, d.head_dim_k, d.head_dim_v, d.v_from_k);
     const int units = p.batch * d.num_kv_heads;
-    const int tiles = int(ceil_div(p.top_k, T));
+    const int k_eff = std::max(1, std::min(p.top_k, p.max_len));   // most tokens any request selects
+    const int tiles = int(ceil_div(k_eff, T));
     int splits = int(ceil_div(512, units));  // aim for >= 2 workgroups per CU
     splits = std::max(1, std::min({splits, tiles, kCombineMaxSplits}));
     plan.kind = 0;
     plan.chunk = int(ceil_div(tiles, splits)) * T;
-    plan.splits = int(ceil_div(p.top_k, plan.chunk));
+    plan.splits = int(ceil_div(k_eff, plan.chunk));
     plan.partial_bytes = plan.splits > 1 ? partial_bytes(size_t(p.batch) * p.num_q_heads * plan.splits,
                                                          d.head_dim_v)
                                          : 0;

@@ -311,10 +311,30 @@ tsa_status tsa_lru_plan(tsa_lru* l, int32_t layer, int64_t tag, int32_t n_req,
     l->plan_slot.clear();
     l->plan_index.reserve(pages.size());
     l->plan_slot.reserve(pages.size());
+    // The touches walk a table of millions of keys and slots in random order, so each one would
+    // wait on several cache misses in turn; the loop prefetches the key's slot a few touches
+    // ahead, and that slot's recency and link entries a little later.
+    std::vector<int64_t> tkey(pages.size());
+    for (int32_t r = 0; r < n_req; ++r)
+        for (int32_t i = first[size_t(r)]; i < first[size_t(r) + 1]; ++i)
+            tkey[size_t(i)] = key_at(r, pages[size_t(i)]);
+    constexpr size_t kAheadKey = 16, kAheadSlot = 8;
+    const size_t n_touch = tkey.size();
     for (int32_t r = 0; r < n_req; ++r)
         for (int32_t i = first[size_t(r)]; i < first[size_t(r) + 1]; ++i) {
-            const int32_t page = pages[size_t(i)];
-            const int64_t key = key_at(r, page);
+            const size_t q = size_t(i);
+            if (q + kAheadKey < n_touch) __builtin_prefetch(&l->slot_of[size_t(tkey[q + kAheadKey])]);
+            if (q + kAheadSlot < n_touch) {
+                const int32_t s2 = l->slot_of[size_t(tkey[q + kAheadSlot])];
+                if (s2 >= 0) {
+                    __builtin_prefetch(&l->pins[size_t(s2)], 1);
+                    __builtin_prefetch(&l->prev[size_t(s2)], 1);
+                    __builtin_prefetch(&l->next[size_t(s2)], 1);
+                    __builtin_prefetch(&l->touched_at[size_t(s2)], 1);
+                }
+            }
+            const int32_t page = pages[q];
+            const int64_t key = tkey[q];
             int32_t slot = l->slot_of[size_t(key)];
             if (slot >= 0) {
                 ++l->hits;
@@ -338,7 +358,17 @@ tsa_status tsa_lru_release(tsa_lru* l, int64_t tag) {
     if (!l) return fail(TSA_ERR_INVALID, "null argument");
     auto it = l->held.find(tag);
     if (it == l->held.end()) return fail(TSA_ERR_INVALID, "tag not held");
-    for (int32_t slot : it->second) l->unpin(slot);
+    const std::vector<int32_t>& hold = it->second;
+    for (size_t i = 0; i < hold.size(); ++i) {
+        if (i + 8 < hold.size()) {      // random slots: fetch their entries ahead of the unpin
+            const size_t s2 = size_t(hold[i + 8]);
+            __builtin_prefetch(&l->pins[s2], 1);
+            __builtin_prefetch(&l->prev[s2], 1);
+            __builtin_prefetch(&l->next[s2], 1);
+            __builtin_prefetch(&l->touched_at[s2], 0);
+        }
+        l->unpin(hold[i]);
+    }
     l->held.erase(it);
     return TSA_OK;
     TSA_GUARD_END

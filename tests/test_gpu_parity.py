@@ -37,12 +37,15 @@ def tsa():
 _STAGED = {}
 
 
-def staged(name, **kw):
+def staged(name, wreplace=None, **kw):
+    """Stage workload `name` (with fields replaced by `wreplace`), cached across tests."""
+    import dataclasses
     from top_sparse_attention_amd import workload
-    key = (name, tuple((k, v.tobytes() if isinstance(v, np.ndarray) else v) for k, v in sorted(kw.items())))
+    wr = tuple(sorted((wreplace or {}).items()))
+    key = (name, wr, tuple((k, v.tobytes() if isinstance(v, np.ndarray) else v) for k, v in sorted(kw.items())))
     if key not in _STAGED:
-        print(f"[stage] {name} {kw}", flush=True)
-        _STAGED[key] = workload.stage(synth.get(name), **kw)
+        print(f"[stage] {name} {dict(wr)} {kw}", flush=True)
+        _STAGED[key] = workload.stage(dataclasses.replace(synth.get(name), **dict(wr)), **kw)
     return _STAGED[key]
 
 
@@ -181,6 +184,20 @@ def test_multihead_indexer_page_sizes(tsa, P, name, heads):
     lens = np.array([1, 47, 48, 49, 200, 777], dtype=np.int32)
     st = staged(name, lens=lens, page_size=P, index_heads=heads)
     _check_scores(st, _scores_gpu(tsa, st), range(len(lens)))
+
+
+@pytest.mark.parametrize("D,P,heads", [(256, 64, 1), (256, 64, 64), (256, 8, 4), (32, 1, 2), (128, 1, 1)])
+def test_indexer_dims_and_small_pages(tsa, D, P, heads):
+    """index_dim 256 on the streaming kernel (one head and 64 heads), and pages below 16 tokens,
+    down to one token per page, on the register kernel; then the whole step."""
+    lens = np.array([1, 100, 1000, 3001], dtype=np.int32)
+    st = staged("gqa_b32_8k", wreplace={"index_dim": D}, lens=lens, page_size=P, index_heads=heads)
+    sc = _scores_gpu(tsa, st)
+    _check_scores(st, sc, range(len(lens)))
+    st.step(append=False)
+    torch.cuda.synchronize()
+    for b in range(len(lens)):
+        _check_request(st, b, sc)
 
 
 def test_multihead_indexer_rejects_too_many_heads(tsa):

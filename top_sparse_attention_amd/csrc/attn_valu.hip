@@ -399,6 +399,14 @@ AttnPlan plan_attention(const tsa_kv_pool& pool, const tsa_decode_params& p) {
                                              : 0;
         return plan;
     }
+    if (gqa_mfma_applicable(pool, p)) {
+        plan.kind = 2;
+        plan.chunk = gqa_mfma_chunk(pool, p, &plan.splits);
+        plan.partial_bytes = plan.splits > 1 ? partial_bytes(size_t(p.batch) * p.num_q_heads * plan.splits,
+                                                             d.head_dim_v)
+                                             : 0;
+        return plan;
+    }
     const int G = p.num_q_heads / d.num_kv_heads;
     const int T = pick_tile(G, d.head_dim_k, d.head_dim_v, d.v_from_k);
     const int units = p.batch * d.num_kv_heads;
@@ -458,6 +466,9 @@ hipError_t launch_attention(const tsa_kv_pool& pool, int layer, const tsa_decode
     if (plan.kind == 1) {
         e = launch_attention_mfma(pool, layer, p, plan, q, topk, page_table, max_pages, seq_lens,
                                   out, a.part_ml, a.part_acc, s);
+    } else if (plan.kind == 2) {
+        e = launch_attention_gqa(pool, layer, p, plan, q, topk, page_table, max_pages, seq_lens,
+                                 out, a.part_ml, a.part_acc, s);
     } else {
         e = launch_valu(a, pool, p, plan, s);
     }

@@ -68,7 +68,7 @@ hipError_t launch_topk(const tsa_decode_params& p, const float* scores, int ld,
 
 // Attention planning: how the selected tokens are split across workgroups.
 struct AttnPlan {
-    int kind = 0;         // 0 = VALU grouped-query kernel, 1 = MFMA latent kernel
+    int kind = 0;         // 0 = VALU grouped-query kernel, 1 = MFMA latent kernel, 2 = MFMA grouped-query
     int splits = 1;       // workgroups per (request, KV head) along the selected tokens
     int chunk = 0;        // selected tokens per split
     size_t partial_bytes = 0;
@@ -82,6 +82,13 @@ hipError_t launch_attention_mfma(const tsa_kv_pool& pool, int layer, const tsa_d
                                  const AttnPlan& plan, const void* q, const int32_t* topk,
                                  const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                                  float* out, float* part_ml, float* part_acc, hipStream_t s);
+// Matrix-core kernel for grouped-query shapes (128-dim keys and values, up to 16 q heads per KV head).
+bool gqa_mfma_applicable(const tsa_kv_pool& pool, const tsa_decode_params& p);
+int gqa_mfma_chunk(const tsa_kv_pool& pool, const tsa_decode_params& p, int* splits);
+hipError_t launch_attention_gqa(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
+                                const AttnPlan& plan, const void* q, const int32_t* topk,
+                                const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                                float* out, float* part_ml, float* part_acc, hipStream_t s);
 hipError_t launch_attention(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                             const AttnPlan& plan, const void* q, const int32_t* topk,
                             const int32_t* page_table, int max_pages, const int32_t* seq_lens,

@@ -40,6 +40,14 @@ def _src_hash(name: str) -> str:
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
+def _has_traffic(key: str) -> bool:
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        return key in json.load(open(p))
+    except Exception:
+        return False
+
+
 def _traffic(kernel_src: str, key: str):
     """Counter-measured HBM bytes per launch from a committed profile summary, or None when the
     kernel source changed since the counters were taken."""
@@ -102,6 +110,16 @@ def _cpu_model() -> str:
 
 
 CALIB_KERNEL = "bitwise_not"   # torch's elementwise kernel name for the calibration copy
+def _attn_src(w) -> str:
+    """Source file of the attention kernel the library picks for workload w (for traffic keys)."""
+    if w.v_from_k:
+        return "attn_mfma.hip"
+    G = w.num_q_heads // w.num_kv_heads
+    if w.head_dim_k == 128 and w.head_dim_v == 128 and G <= 16:
+        return "attn_gqa.hip"
+    return "attn_valu.hip"
+
+
 TRAFFIC_KERNELS = {            # profiles/traffic.json key prefix -> (kernel-name test, source)
     "indexer_score": (lambda n: "indexer_score" in n, "indexer_score.hip"),
     "attention": (lambda n: "attn" in n and "combine" not in n, None),
@@ -167,7 +185,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, mib: int):
         fk = np.mean([v for k in names for v in fetch[k]])
         wk = np.mean([v for k in write if match(k) for v in write[k]])
         if src is None:
-            src = "attn_mfma.hip" if (w is not None and w.v_from_k) else "attn_valu.hip"
+            src = _attn_src(w) if w is not None else "attn_valu.hip"
         doc[f"{key}/{workload}"] = {
             "kernel": names[0][:120], "src_sha256_16": _src_hash(src),
             "fetch_kib": round(float(fk), 1), "write_kib": round(float(wk), 1),
@@ -496,18 +514,37 @@ def main():
                      B * w.num_q_heads * w.head_dim_v * 4 + B * w.top_k * 4)
     attn_flops = float(2 * n_sel.sum() * w.num_q_heads * (w.head_dim_k + w.head_dim_v))
 
-    attn_src = "attn_mfma.hip" if w.v_from_k else "attn_valu.hip"
+    attn_src = _attn_src(w)
+    # Bytes HBM must deliver at the least.  Requests of a shared-prefix workload alias the same
+    # prefix pages, so a row several requests read is counted once; elsewhere this equals the
+    # algorithmic count.
+    idx_unique, attn_unique = idx_bytes, attn_bytes
+    grp, plen = synth.prefix_groups(w)
+    if grp is not None:
+        shared_tok = (int(plen[0]) // w.page_size) * w.page_size
+        idx_unique = int((lens.sum() - (B - 1) * shared_tok) * 2 * D_I + lens.sum() * 4)
+        tk = st.topk.cpu().numpy().astype(np.int64)
+        P = w.page_size
+        slots = [st.table[b][tk[b][tk[b] >= 0] // P].astype(np.int64) * P + tk[b][tk[b] >= 0] % P
+                 for b in range(B)]
+        n_unique = int(np.unique(np.concatenate(slots)).size)
+        attn_unique = int(attn_bytes - n_sel.sum() * row + n_unique * row)
 
-    def roof(nbytes, ms, src, key):
-        gbs = nbytes / (ms * 1e-3) / 1e9
+    def roof(nbytes, unique, ms, src, key):
+        gbs = unique / (ms * 1e-3) / 1e9
         traffic = _traffic(src, key)
-        if key.startswith("attention/") and traffic is not None:
-            # the timed attention call is the gather kernel plus the split combine
+        if key.startswith("attention/") and traffic is not None and _has_traffic(f"combine/{w.name}"):
+            # the timed attention call is the gather kernel plus the split combine (a workload
+            # whose counter run saw no combine launch has one split)
             comb = _traffic("attn_valu.hip", f"combine/{w.name}")
             traffic = None if comb is None else traffic + comb
-        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes": nbytes, "kernel_ms": round(ms, 5)}
+        r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+             "algorithmic_bytes": nbytes, "kernel_ms": round(ms, 5)}
+        if unique != nbytes:
+            r["unique_bytes"] = unique
+            r["bytes_basis"] = "unique: rows aliased by several requests counted once"
+        return r
 
     out = {
         "metric": "sparse decode attention tokens/s + achieved HBM GB/s vs peak, 32k ctx top-2048",
@@ -531,9 +568,9 @@ def main():
                        "topk": round(t_topk, 5), "attention": round(t_attn, 5)},
         "kernel_timing": "HIP events between kernels on the launch stream, over a second pass of "
                          "the same steps (the throughput pass has no events between kernels)",
-        "roofline": dict(roof(idx_bytes, t_index, "indexer_score.hip", f"indexer_score/{w.name}"),
+        "roofline": dict(roof(idx_bytes, idx_unique, t_index, "indexer_score.hip", f"indexer_score/{w.name}"),
                          flops=idx_flops, tflops=round(idx_flops / (t_index * 1e-3) / 1e12, 2)),
-        "roofline_attention": dict(roof(attn_bytes, t_attn, attn_src, f"attention/{w.name}"),
+        "roofline_attention": dict(roof(attn_bytes, attn_unique, t_attn, attn_src, f"attention/{w.name}"),
                                    flops=attn_flops,
                                    tflops=round(attn_flops / (t_attn * 1e-3) / 1e12, 2)),
         "cpu_baseline": None,

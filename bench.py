@@ -318,7 +318,7 @@ def bench_tier(args):
     out = torch.empty((R, w.num_q_heads, w.head_dim_v), dtype=torch.float32, device="cuda")
     total_steps = args.warmup + args.steps
     centres, pos_all = {}, []
-    for step in range(total_steps):
+    for step in range(total_steps if args.tier_positions == "drawn" else 0):
         layer_pos = []
         for layer in range(NL):
             a = np.empty((R, k), dtype=np.int32)
@@ -328,6 +328,36 @@ def bench_tier(args):
             layer_pos.append(a)
         pos_all.append(layer_pos)
     pos_dev = [[torch.from_numpy(a).cuda() for a in lp] for lp in pos_all]
+    use_indexer = args.tier_positions == "indexer"
+    if use_indexer:
+        # HiSparse's flow: the indexer keys of every token stay in HBM (256 B per token), each
+        # layer scores them and selects its top-k on the GPU, and the selection is copied to the
+        # host, which plans the fetch.  Keys are random integers in [-4, 4]; each layer's query
+        # keeps 90 % of its dims from one step to the next, so selections drift over steps as
+        # a slowly changing hidden state would make them.
+        D_I = 128
+        ipool = KvPool(R * npr, P, 1, 8, 8, num_layers=NL, v_from_k=True, index_dim=D_I)
+        itab, _, _ = ipool.build_tables(np.full(R, L, dtype=np.int32), npr)
+        itab_dev = torch.from_numpy(itab).cuda()
+        gd = torch.Generator(device="cuda").manual_seed(args.seed)
+        per_layer = ipool.idx.numel() // NL
+        for l in range(NL):
+            ipool.idx[l * per_layer:(l + 1) * per_layer].copy_(
+                torch.randint(-4, 5, (per_layer,), generator=gd, device="cuda", dtype=torch.int16))
+        rng = np.random.default_rng(args.seed + 1)
+        qcur = rng.integers(-4, 5, size=(NL, R, D_I))
+        qidx_all = []
+        for step in range(total_steps):
+            if step:
+                redraw = rng.random((NL, R, D_I)) < 0.1
+                qcur = np.where(redraw, rng.integers(-4, 5, size=(NL, R, D_I)), qcur)
+            qidx_all.append(torch.from_numpy(qcur.astype(np.float32)).to(torch.bfloat16).cuda())
+        iparams = decode_params(R, w.num_q_heads, k, L, w.sm_scale)
+        iws = torch.empty(max(workspace_bytes(ipool, iparams), 256), dtype=torch.uint8, device="cuda")
+        iw = torch.ones(1, dtype=torch.float32, device="cuda")
+        sel_dev = [torch.empty((R, k), dtype=torch.int32, device="cuda") for _ in range(2)]
+        sel_host = [torch.empty((R, k), dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        sel_ready = [torch.cuda.Event() for _ in range(2)]
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     table_dev = [torch.full((R, unpr), -1, dtype=torch.int32, device="cuda") for _ in range(2)]
@@ -340,8 +370,17 @@ def bench_tier(args):
     def run_step(step, timed):
         nonlocal gidx
         for layer in range(NL):
+            if use_indexer:
+                sd, sh = sel_dev[gidx & 1], sel_host[gidx & 1]
+                tsa.indexer_topk(ipool, layer, iparams, qidx_all[step][layer], iw, itab_dev, lens_dev, sd, iws)
+                sh.copy_(sd, non_blocking=True)
+                sel_ready[gidx & 1].record(main)
+                sel_ready[gidx & 1].synchronize()
+                positions, pos_layer = sh.numpy(), sd
+            else:
+                positions, pos_layer = pos_all[step][layer], pos_dev[step][layer]
             h0 = time.perf_counter()
-            tier.plan(layer, gidx, pos_all[step][layer], table=False)
+            tier.plan(layer, gidx, positions, table=False)
             h1 = time.perf_counter()
             if gidx - 2 in done:
                 side.wait_event(done[gidx - 2])
@@ -354,7 +393,7 @@ def bench_tier(args):
             e0 = torch.cuda.Event(enable_timing=True) if timed else None
             if timed:
                 e0.record(main)
-            tsa.sparse_attn_gather(cache, 0, params, q, pos_dev[step][layer], table_dev[gidx & 1], lens_dev,
+            tsa.sparse_attn_gather(cache, 0, params, q, pos_layer, table_dev[gidx & 1], lens_dev,
                                    out, ws)
             ev = torch.cuda.Event(enable_timing=timed)
             ev.record(main)
@@ -387,7 +426,8 @@ def bench_tier(args):
         "config": {"workload": w.name, "requests": R, "context": L, "layers": NL, "top_k": k,
                    "page_size": P, "cache_unit": args.tier_unit, "cache_slots": CP,
                    "cache_bytes": CP * UP * row * 4, "logical_pages": keys, "q_heads": w.num_q_heads,
-                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim_k, "parallelism": "none"},
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim_k, "parallelism": "none",
+                   "positions": args.tier_positions},
         "tier": {"hit_rate": round(hits / max(hits + misses, 1), 4), "hits": hits, "misses": misses,
                  "h2d_GBps": round(h2d / elapsed / 1e9, 2), "h2d_bytes_per_step": h2d // args.steps,
                  "attention_ms_per_layer": round(attn_ms, 4),
@@ -408,6 +448,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--tier-requests", type=int, default=16,
                     help="requests of the tiered workload (the full 256 needs 128 GiB of pinned memory)")
+    ap.add_argument("--tier-positions", choices=("drawn", "indexer"), default="drawn",
+                    help="tiered workload: positions from the seeded locality generator, or from an "
+                         "indexer top-k per layer over HBM-resident indexer keys (copied to the host)")
     ap.add_argument("--tier-unit", choices=("page", "token"), default="page",
                     help="cache unit of the tiered workload: whole pages or single token rows")
     ap.add_argument("--mla-modes", action="store_true",

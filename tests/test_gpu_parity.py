@@ -200,6 +200,23 @@ def test_indexer_dims_and_small_pages(tsa, D, P, heads):
         _check_request(st, b, sc)
 
 
+@pytest.mark.parametrize("wrep", [
+    {"head_dim_k": 256, "head_dim_v": 256},                       # matrix cores, 256-dim heads
+    {"num_kv_heads": 1},                                          # 32 q heads on one KV head: vector ALUs
+    {"head_dim_k": 128, "head_dim_v": 64, "v_from_k": True},      # values alias keys: vector ALUs
+    {"head_dim_k": 96, "head_dim_v": 96},                         # dims no matrix-core kernel takes
+])
+def test_attention_kernel_shapes(tsa, wrep):
+    """Each attention kernel and shape class through the whole step on a few requests."""
+    lens = np.array([5, 700, 3001], dtype=np.int32)
+    st = staged("gqa_b32_8k", wreplace=wrep, lens=lens, page_size=64)
+    sc = _scores_gpu(tsa, st)
+    st.step(append=False)
+    torch.cuda.synchronize()
+    for b in range(len(lens)):
+        _check_request(st, b, sc)
+
+
 def test_multihead_indexer_rejects_too_many_heads(tsa):
     st = staged("tiny_b5", lens=np.array([30, 40], dtype=np.int32), page_size=8, index_heads=8)
     p = tsa.decode_params(2, st.params.num_q_heads, st.params.top_k, st.params.max_len,

@@ -1,5 +1,6 @@
 // Sparse gather-attention on the matrix cores for grouped-query shapes: up to 16 query heads per
-// KV head, keys and values of 128 dims stored apart.
+// KV head, keys and values stored apart, head dims (keys, values) of (64, 64), (128, 128),
+// (192, 128) or (256, 256).
 //
 // GLM5.3 sparse-attention page: SDPA runs over only the tokens the indexer kept (opening
 // paragraph), one selection for every head (lightning-indexer paragraph).  For query head h of
@@ -10,68 +11,83 @@
 // workgroup barrier.  It writes the unit's physical rows to LDS, then streams 32-row tiles of K
 // and V through a private ring of LDS slots with global-to-LDS loads (all but one slot in flight
 // while the oldest is consumed).  Per tile:
-//   S^T = K_tile Q^T   2 row blocks x 4 k-steps of mfma_f32_16x16x32_bf16; tokens are rows, the
+//   S^T = K_tile Q^T   2 row blocks x DK/32 k-steps of mfma_f32_16x16x32_bf16; tokens are rows, the
 //                      G heads are columns padded to 16 (zero queries, never written out);
 //   softmax            online, per head: running max (log2 units) and sum, with the accumulator
 //                      rescaled when the max moves;
-//   O^T += V^T P^T     8 output blocks of 16 dims, each with P split into bf16 hi + lo (two
+//   O^T += V^T P^T     DV/16 output blocks of 16 dims, each with P split into bf16 hi + lo (two
 //                      MFMAs, fp32-like accuracy).  V^T comes straight from the tile through the
 //                      LDS transpose read; the contraction index k = 8 g + i of lane group g
 //                      stands for token (i < 4 ? 4 g + i : 16 + 4 g + i - 4), which is exactly
 //                      where the S^T accumulator left that lane's probabilities, so P needs no
 //                      shuffle.
-// Rows are stored with their 16-byte chunks XOR-swizzled by row, so the 16 rows an MFMA operand
-// read touches fall on distinct LDS banks.
+// Rows are stored with their 16-byte chunks XOR-swizzled by row, so the rows an MFMA operand read
+// touches fall on distinct LDS banks (on 16 bank groups; 64-dim rows, 8 chunks wide, pair up).
 #include "tsa_internal.h"
 #include "mfma_lds.h"
 
 namespace {
 
-constexpr int kD = 128;                          // key and value dims this kernel takes
 constexpr int kMaxG = 16;                        // query heads per KV head (one MFMA column block)
 constexpr int kTileG = 32;                       // rows per tile
-// Two tiles per wave and one wave per workgroup: 36 KiB of LDS each, so four waves share a CU
-// and a CU picks up a new unit as soon as any of its four finishes.  Measured on the
+// Two tiles per wave and one wave per workgroup (36 KiB of LDS at 128 dims, so four waves share
+// a CU, and a CU picks up a new unit as soon as any of its waves finishes).  Measured on the
 // 128-request shared-prefix workload: 60 us, against 70-98 us for 3-4 tiles per wave or 2-4
 // units per workgroup (fewer waves per CU, or units that hold their CU until the slowest of the
 // group is done).
-constexpr int kRingG = 2;                        // tiles per wave in LDS
+constexpr int kRingG = 2;                        // tiles per wave in LDS (the loop assumes 2)
 constexpr int kUnitsPerWg = 1;                   // waves (units) per workgroup
 constexpr int kRowsMaxG = 1024;                  // selected rows per unit (its LDS row list)
-constexpr int kRowBytes = kD * 2;                // 256
-constexpr int kHalfBytes = kTileG * kRowBytes;   // K (or V) part of a tile: 8 KiB
-constexpr int kTileBytesG = 2 * kHalfBytes;
-constexpr int kLoadsHalf = kHalfBytes / 1024;    // wave-wide 1 KiB loads per half: 8
-constexpr int kLoadsTile = 2 * kLoadsHalf;
-constexpr int kWaveLds = kRingG * kTileBytesG + kRowsMaxG * 4;
 constexpr float kLog2eG = 1.4426950408889634f;
-static_assert(kLoadsTile * (kRingG - 1) < 64, "vmcnt range");
+
+template <int DK, int DV>
+struct GqaGeo {
+    static constexpr int kChunksK = DK / 8, kChunksV = DV / 8;        // 16-byte chunks per row
+    static constexpr int kRowBytesK = DK * 2, kRowBytesV = DV * 2;
+    static constexpr int kHalfK = kTileG * kRowBytesK, kHalfV = kTileG * kRowBytesV;
+    static constexpr int kTileBytes = kHalfK + kHalfV;
+    static constexpr int kLoadsK = kHalfK / 1024, kLoadsV = kHalfV / 1024;   // wave-wide 1 KiB loads
+    static constexpr int kLoadsTile = kLoadsK + kLoadsV;
+    static constexpr int kWaveLds = kRingG * kTileBytes + kRowsMaxG * 4;
+    static_assert(kHalfK % 1024 == 0 && kHalfV % 1024 == 0, "whole wave loads per tile half");
+    static_assert(kLoadsTile < 64, "vmcnt range");
+    static_assert(DK % 32 == 0 && DV % 16 == 0, "MFMA k-steps and output blocks");
+};
+
+// stored chunk position of logical chunk c in a tile row r of C chunks (an involution on c):
+// full groups of 16 chunks XOR the low 4 bits of the row, a trailing group of 8 the low 3
+template <int C>
+__device__ __forceinline__ int swz(int r, int c) {
+    if constexpr (C % 16 == 0) return c ^ (r & 15);
+    else if constexpr (C == 8) return c ^ (r & 7);
+    else return c < (C & ~15) ? (c ^ (r & 15)) : (c ^ (r & 7));
+}
 
 struct GqaArgs {
-    const uint16_t* q;          // [B][Hq][128]
+    const uint16_t* q;          // [B][Hq][DK]
     const int32_t* topk;        // [B][k]
     const int32_t* page_table;
     const int32_t* seq_lens;
-    const uint16_t* kpool;      // layer bases; row (slot, g) at (slot * hkv + g) * 128
+    const uint16_t* kpool;      // layer bases; row (slot, g) at (slot * hkv + g) * DK (V: * DV)
     const uint16_t* vpool;
-    float* out;                 // [B][Hq][128]
+    float* out;                 // [B][Hq][DV]
     float* part_ml;             // [B][Hq][S][2]
-    float* part_acc;            // [B][Hq][S][128]
+    float* part_acc;            // [B][Hq][S][DV]
     int k, max_pages, page_size, num_pages, max_len, hq, hkv, splits, chunk, n_units;
     float scale_log2;           // sm_scale * log2(e)
 };
 
-// stored chunk position of logical chunk c (of 16) in tile row r; an involution on c
-__device__ __forceinline__ int swz16(int r, int c) { return c ^ (r & 15); }
-
+template <int DK, int DV>
 __global__ void __launch_bounds__(64 * kUnitsPerWg) attn_gqa_kernel(GqaArgs a) {
+    using Geo = GqaGeo<DK, DV>;
+    constexpr int CK = Geo::kChunksK, CV = Geo::kChunksV;
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int unit = blockIdx.x * kUnitsPerWg + wave;
     if (unit >= a.n_units) return;                      // uniform: the whole wave
-    unsigned char* ring = smem + wave * kWaveLds;
-    int32_t* rows = reinterpret_cast<int32_t*>(ring + kRingG * kTileBytesG);
+    unsigned char* ring = smem + wave * Geo::kWaveLds;
+    int32_t* rows = reinterpret_cast<int32_t*>(ring + kRingG * Geo::kTileBytes);
     const int s_idx = unit % a.splits;
     const int g = (unit / a.splits) % a.hkv;
     const int b = unit / (a.splits * a.hkv);
@@ -88,12 +104,12 @@ __global__ void __launch_bounds__(64 * kUnitsPerWg) attn_gqa_kernel(GqaArgs a) {
     // queries, the B operand of S^T = K Q^T: lane (j16, g16) holds dims 32 ks + 8 g16 .. of
     // head h0 + j16
     const int h0 = g * G;
-    uint4 qreg[kD / 32];
+    uint4 qreg[DK / 32];
     {
         const bool hv = j16 < G;
-        const uint4* src = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.hq + h0 + (hv ? j16 : 0)) * kD);
+        const uint4* src = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.hq + h0 + (hv ? j16 : 0)) * DK);
 #pragma unroll
-        for (int ks = 0; ks < kD / 32; ++ks) qreg[ks] = hv ? src[4 * ks + g16] : make_uint4(0, 0, 0, 0);
+        for (int ks = 0; ks < DK / 32; ++ks) qreg[ks] = hv ? src[4 * ks + g16] : make_uint4(0, 0, 0, 0);
     }
     // physical rows (slot * hkv + g) of the unit's positions, -1 when absent (fetched from row 0
     // like any other and masked out of the softmax); all position loads, then all page loads
@@ -122,59 +138,62 @@ __global__ void __launch_bounds__(64 * kUnitsPerWg) attn_gqa_kernel(GqaArgs a) {
     __builtin_amdgcn_wave_barrier();
 
     const uint32_t ring_base = lds_addr(ring);
-    // tile t into slot t % kRingG: load i of each half fills rows 4 i .. 4 i + 3, lane = stored
-    // chunk position, so each lane fetches the logical chunk that belongs there
+    // tile t into slot t % kRingG: load i of a half fills its 1 KiB at 1024 i, lane l the 16 bytes
+    // at chunk position 64 i + l of the row-major stored layout, so each lane fetches the logical
+    // chunk that belongs there
     auto issue_tile = [&](int t) {
-        const uint32_t slot = ring_base + uint32_t((t % kRingG) * kTileBytesG);
+        const uint32_t slot = ring_base + uint32_t((t % kRingG) * Geo::kTileBytes);
 #pragma unroll
-        for (int i = 0; i < kLoadsHalf; ++i) {
-            const int r = 4 * i + (lane >> 4);
+        for (int i = 0; i < Geo::kLoadsK; ++i) {
+            const int pc = 64 * i + lane, r = pc / CK;
             const int32_t row = rows[t * kTileG + r];
-            const int64_t off = int64_t(row < 0 ? 0 : row) * kD + swz16(r, lane & 15) * 8;
-            load_lds16(a.kpool + off, __builtin_amdgcn_readfirstlane(slot + uint32_t(i * 1024)));
-            load_lds16(a.vpool + off, __builtin_amdgcn_readfirstlane(slot + uint32_t(kHalfBytes + i * 1024)));
+            load_lds16(a.kpool + int64_t(row < 0 ? 0 : row) * DK + swz<CK>(r, pc % CK) * 8,
+                       __builtin_amdgcn_readfirstlane(slot + uint32_t(i * 1024)));
+        }
+#pragma unroll
+        for (int i = 0; i < Geo::kLoadsV; ++i) {
+            const int pc = 64 * i + lane, r = pc / CV;
+            const int32_t row = rows[t * kTileG + r];
+            load_lds16(a.vpool + int64_t(row < 0 ? 0 : row) * DV + swz<CV>(r, pc % CV) * 8,
+                       __builtin_amdgcn_readfirstlane(slot + uint32_t(Geo::kHalfK + i * 1024)));
         }
     };
     // lane-constant byte offsets in a tile: K operand of row j16 (+16 rows for the second
     // block), chunk 4 ks + g16; V^T transpose reads of rows r0 and r0 + 16, dims 16 db + e0 ..
-    int koff[kD / 32], voff[kD / 16];
+    int koff[DK / 32], voff[DV / 16];
 #pragma unroll
-    for (int ks = 0; ks < kD / 32; ++ks) koff[ks] = j16 * kRowBytes + swz16(j16, 4 * ks + g16) * 16;
+    for (int ks = 0; ks < DK / 32; ++ks) koff[ks] = j16 * Geo::kRowBytesK + swz<CK>(j16, 4 * ks + g16) * 16;
     {
         const int r0 = 4 * g16 + (j16 >> 2), e0 = 4 * (j16 & 3);
 #pragma unroll
-        for (int db = 0; db < kD / 16; ++db)
-            voff[db] = kHalfBytes + r0 * kRowBytes + swz16(r0, 2 * db + (e0 >> 3)) * 16 + (e0 & 7) * 2;
+        for (int db = 0; db < DV / 16; ++db)
+            voff[db] = Geo::kHalfK + r0 * Geo::kRowBytesV + swz<CV>(r0, 2 * db + (e0 >> 3)) * 16 + (e0 & 7) * 2;
     }
 
     for (int t = 0; t < kRingG - 1 && t < n_tiles; ++t) issue_tile(t);
     float m_run = -INFINITY;     // head j16: running max of the scaled logits (log2 units)
     float l_run = 0.f;           // this lane's share of head j16's running sum
-    f32x4 acc[kD / 16];          // O^T[16 db + 4 g16 + r][head j16], unnormalised
+    f32x4 acc[DV / 16];          // O^T[16 db + 4 g16 + r][head j16], unnormalised
 #pragma unroll
-    for (int db = 0; db < kD / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < DV / 16; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int t = 0; t < n_tiles; ++t) {
-        // the slot tile t + kRingG - 1 takes was read (and consumed) in the previous iteration
-        if (t + kRingG - 1 < n_tiles) {
-            issue_tile(t + kRingG - 1);
-            wait_vm<kLoadsTile * (kRingG - 1)>();
-        } else if (kRingG > 2 && t + 2 < n_tiles) {
-            wait_vm<kLoadsTile * 2>();
-        } else if (t + 1 < n_tiles) {
-            wait_vm<kLoadsTile>();
+        // the slot tile t + 1 takes held tile t - 1, read (and consumed) in the previous iteration
+        if (t + 1 < n_tiles) {
+            issue_tile(t + 1);
+            wait_vm<Geo::kLoadsTile>();      // tile t landed, tile t + 1 in flight
         } else {
             wait_vm<0>();
         }
-        const unsigned char* tile = ring + (t % kRingG) * kTileBytesG;
+        const unsigned char* tile = ring + (t % kRingG) * Geo::kTileBytes;
         // tokens of the tile that are present
         const uint32_t live = uint32_t(__ballot(lane < kTileG && t * kTileG + lane < n &&
                                                 rows[t * kTileG + (lane & (kTileG - 1))] >= 0));
         f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int ks = 0; ks < kD / 32; ++ks) {
+        for (int ks = 0; ks < DK / 32; ++ks) {
             const uint4 k0 = *reinterpret_cast<const uint4*>(tile + koff[ks]);
-            const uint4 k1 = *reinterpret_cast<const uint4*>(tile + koff[ks] + 16 * kRowBytes);
+            const uint4 k1 = *reinterpret_cast<const uint4*>(tile + koff[ks] + 16 * Geo::kRowBytesK);
             const bf16x8 qb = as_bf16x8(qreg[ks]);
             s[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k0), qb, s[0], 0, 0, 0);
             s[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(k1), qb, s[1], 0, 0, 0);
@@ -211,10 +230,10 @@ __global__ void __launch_bounds__(64 * kUnitsPerWg) attn_gqa_kernel(GqaArgs a) {
         const bf16x8 phi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
         const bf16x8 plo = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
 #pragma unroll
-        for (int db = 0; db < kD / 16; ++db) {
+        for (int db = 0; db < DV / 16; ++db) {
             const unsigned char* p0 = tile + voff[db];
             const uint2 w0 = lds_read_tr16(p0);
-            const uint2 w1 = lds_read_tr16(p0 + 16 * kRowBytes);
+            const uint2 w1 = lds_read_tr16(p0 + 16 * Geo::kRowBytesV);
             const bf16x8 va = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
             acc[db] = acc[db] * alpha;
             acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[db], 0, 0, 0);
@@ -227,16 +246,16 @@ __global__ void __launch_bounds__(64 * kUnitsPerWg) attn_gqa_kernel(GqaArgs a) {
     const int h = h0 + j16;
     if (a.splits == 1) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        float* o = a.out + (int64_t(b) * a.hq + h) * kD;
+        float* o = a.out + (int64_t(b) * a.hq + h) * DV;
 #pragma unroll
-        for (int db = 0; db < kD / 16; ++db)
+        for (int db = 0; db < DV / 16; ++db)
             *reinterpret_cast<float4*>(o + db * 16 + 4 * g16) =
                 make_float4(acc[db][0] * inv, acc[db][1] * inv, acc[db][2] * inv, acc[db][3] * inv);
     } else {
         const int64_t pidx = (int64_t(b) * a.hq + h) * a.splits + s_idx;
-        float* o = a.part_acc + pidx * kD;
+        float* o = a.part_acc + pidx * DV;
 #pragma unroll
-        for (int db = 0; db < kD / 16; ++db)
+        for (int db = 0; db < DV / 16; ++db)
             *reinterpret_cast<float4*>(o + db * 16 + 4 * g16) =
                 make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
         if (g16 == 0) {
@@ -249,11 +268,36 @@ __global__ void __launch_bounds__(64 * kUnitsPerWg) attn_gqa_kernel(GqaArgs a) {
 
 }  // namespace
 
+namespace {
+
+// LDS bytes of one wave for a shape the kernel takes, 0 for others
+size_t gqa_wave_lds(int dk, int dv) {
+    if (dk == 64 && dv == 64) return GqaGeo<64, 64>::kWaveLds;
+    if (dk == 128 && dv == 128) return GqaGeo<128, 128>::kWaveLds;
+    if (dk == 192 && dv == 128) return GqaGeo<192, 128>::kWaveLds;
+    if (dk == 256 && dv == 256) return GqaGeo<256, 256>::kWaveLds;
+    return 0;
+}
+
+template <int DK, int DV>
+hipError_t launch_gqa(const GqaArgs& a, hipStream_t s) {
+    auto kern = attn_gqa_kernel<DK, DV>;
+    const size_t smem = size_t(kUnitsPerWg) * GqaGeo<DK, DV>::kWaveLds;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    if (e != hipSuccess) return e;
+    const int wgs = (a.n_units + kUnitsPerWg - 1) / kUnitsPerWg;
+    hipLaunchKernelGGL(kern, dim3(wgs), dim3(64 * kUnitsPerWg), smem, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 namespace tsa {
 
 bool gqa_mfma_applicable(const tsa_kv_pool& pool, const tsa_decode_params& p) {
     const tsa_pool_desc& d = pool.d;
-    if (d.v_from_k || d.head_dim_k != kD || d.head_dim_v != kD) return false;
+    if (d.v_from_k || !gqa_wave_lds(d.head_dim_k, d.head_dim_v)) return false;
     if (p.num_q_heads % d.num_kv_heads || p.num_q_heads / d.num_kv_heads > kMaxG) return false;
     if (pool.slots() * int64_t(d.num_kv_heads) >= (int64_t(1) << 31)) return false;   // int32 rows
     int splits = 0;
@@ -267,9 +311,10 @@ int gqa_mfma_chunk(const tsa_kv_pool& pool, const tsa_decode_params& p, int* spl
     const int k_eff = std::max(1, std::min(p.top_k, p.max_len));
     const int tiles = int(ceil_div(k_eff, kTileG));
     const int64_t base = std::max<int64_t>(1, int64_t(p.batch) * pool.d.num_kv_heads);
-    constexpr int kWgPerCu = (160 * 1024) / (kUnitsPerWg * kWaveLds);   // LDS-bound residency
-    constexpr int kCus = 256 * kWgPerCu;                                // workgroup slots
-    const int64_t slots = int64_t(kCus) * kUnitsPerWg;
+    const size_t wave_lds = std::max<size_t>(1, gqa_wave_lds(pool.d.head_dim_k, pool.d.head_dim_v));
+    const int wg_per_cu = std::max<int>(1, int((160 * 1024) / (kUnitsPerWg * wave_lds)));   // LDS-bound
+    const int64_t wg_slots = int64_t(256) * wg_per_cu;
+    const int64_t slots = wg_slots * kUnitsPerWg;
     int s_min = int(std::max<int64_t>(1, ceil_div(slots, base)));
     s_min = std::max(s_min, int(ceil_div(tiles, kRowsMaxG / kTileG)));
     s_min = std::min({s_min, tiles, 64});
@@ -279,7 +324,7 @@ int gqa_mfma_chunk(const tsa_kv_pool& pool, const tsa_decode_params& p, int* spl
         const int chunk_t = int(ceil_div(tiles, s));
         const int sp = int(ceil_div(tiles, chunk_t));
         const int64_t wgs = ceil_div(base * sp, kUnitsPerWg);
-        const double fill = double(wgs) / double(ceil_div(wgs, kCus) * kCus);
+        const double fill = double(wgs) / double(ceil_div(wgs, wg_slots) * wg_slots);
         if (fill > best_fill + 0.02) {
             best_fill = fill;
             best_s = s;
@@ -301,8 +346,8 @@ hipError_t launch_attention_gqa(const tsa_kv_pool& pool, int layer, const tsa_de
     a.page_table = page_table;
     a.seq_lens = seq_lens;
     const int64_t layer_rows = pool.slots() * d.num_kv_heads;
-    a.kpool = static_cast<const uint16_t*>(pool.k) + int64_t(layer) * layer_rows * kD;
-    a.vpool = static_cast<const uint16_t*>(pool.v) + int64_t(layer) * layer_rows * kD;
+    a.kpool = static_cast<const uint16_t*>(pool.k) + int64_t(layer) * layer_rows * d.head_dim_k;
+    a.vpool = static_cast<const uint16_t*>(pool.v) + int64_t(layer) * layer_rows * d.head_dim_v;
     a.out = out;
     a.part_ml = part_ml;
     a.part_acc = part_acc;
@@ -317,13 +362,11 @@ hipError_t launch_attention_gqa(const tsa_kv_pool& pool, int layer, const tsa_de
     a.chunk = plan.chunk;
     a.n_units = p.batch * d.num_kv_heads * plan.splits;
     a.scale_log2 = p.sm_scale * kLog2eG;
-    const size_t smem = size_t(kUnitsPerWg) * kWaveLds;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_gqa_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
-    if (e != hipSuccess) return e;
-    const int wgs = int(ceil_div(a.n_units, kUnitsPerWg));
-    hipLaunchKernelGGL(attn_gqa_kernel, dim3(wgs), dim3(64 * kUnitsPerWg), smem, s, a);
-    return hipGetLastError();
+    if (d.head_dim_k == 64) return launch_gqa<64, 64>(a, s);
+    if (d.head_dim_k == 128) return launch_gqa<128, 128>(a, s);
+    if (d.head_dim_k == 192) return launch_gqa<192, 128>(a, s);
+    if (d.head_dim_k == 256) return launch_gqa<256, 256>(a, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace tsa

@@ -455,6 +455,9 @@ def main():
                     help="cache unit of the tiered workload: whole pages or single token rows")
     ap.add_argument("--mla-modes", action="store_true",
                     help="compare latent attention in MQA mode and MHA mode over context lengths and exit")
+    ap.add_argument("--separate", action="store_true",
+                    help="time the step as separate calls (kv_append, scores, top-k, attention) "
+                         "instead of tsa_decode_step")
     ap.add_argument("--graph", action="store_true",
                     help="time the step as one replay of a captured graph (tsa_step_graph_*)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -517,6 +520,13 @@ def main():
             ev[4].record(stream)
 
     timed = step
+    if st.new_req is not None and len(st.new_req) == B and not args.separate:
+        # the library's whole step: the new token of every request written inside the step
+        # (tsa_decode_step); the kernel-timing pass below runs the same kernels as separate calls
+        k_new, v_new, i_new = st.new_k, st.new_v, st.new_idx
+        timed = lambda: tsa.decode_step(st.pool, 0, st.params, k_new, v_new, i_new, st.q, st.qidx,
+                                        st.widx, st.table_dev, st.lens_dev, st.out, st.workspace,
+                                        topk_out=st.topk, stream=stream)
     if args.graph:
         graph = tsa.StepGraph(st.pool, 0, st.params, st.q, st.qidx, st.widx, st.table_dev, st.lens_dev,
                               st.out, st.workspace, topk_out=st.topk,
@@ -606,7 +616,7 @@ def main():
                    "top_k": w.top_k, "page_size": w.page_size, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim_k": w.head_dim_k, "head_dim_v": w.head_dim_v,
                    "index_dim": D_I, "index_heads": w.index_heads, "parallelism": "none",
-                   "launch": "graph" if args.graph else "eager"},
+                   "launch": "graph" if args.graph else ("separate calls" if args.separate else "tsa_decode_step")},
         "kernels_ms": {"kv_append": round(t_append, 5), "indexer_score": round(t_index, 5),
                        "topk": round(t_topk, 5), "attention": round(t_attn, 5)},
         "kernel_timing": "HIP events between kernels on the launch stream, over a second pass of "

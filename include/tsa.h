@@ -220,6 +220,23 @@ tsa_status tsa_sparse_decode_attn(tsa_kv_pool* pool, int32_t layer, const tsa_de
                                   const int32_t* seq_lens_dev, float* out_dev, int32_t* topk_dev,
                                   void* workspace, size_t ws_bytes, void* stream);
 
+/* The decode step with its own new token: request b's new rows (k_new_dev [B][Hkv][head_dim_k],
+ * v_new_dev [B][Hkv][head_dim_v] or NULL exactly when values alias keys, idx_new_dev
+ * [B][index_dim], all bf16) are written at position seq_lens[b] - 1 (the token being decoded,
+ * already counted in its length) of every request with seq_lens[b] >= 1; then scores, top-k and
+ * attention run as in tsa_sparse_decode_attn, the new token included.  Paged-KV page, section
+ * "Phân trang": the position's page comes from the page table.  Where pages hold at least 16
+ * tokens and index_dim is 32..256, the writes ride in the scoring launch (the new token is
+ * scored from its new row); elsewhere a separate launch writes them first.  A token whose
+ * page-table entry is not a page of the pool is not written, scores -inf and is counted in
+ * bad_dev (nullable, int32, accumulated).  Other arguments and errors as tsa_sparse_decode_attn. */
+tsa_status tsa_decode_step(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                           const void* k_new_dev, const void* v_new_dev, const void* idx_new_dev,
+                           int32_t* bad_dev, const void* q_dev, const void* qidx_dev,
+                           const float* widx_dev, const int32_t* page_table_dev, int32_t max_pages,
+                           const int32_t* seq_lens_dev, float* out_dev, int32_t* topk_dev,
+                           void* workspace, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------------
  * Captured step.  GLM5.3 page, paragraph on serving-engine prefill and decode (the GLM-5.2
  * studies): running the decode step on a fixed graph-execution path lowered the time per output

@@ -21,7 +21,7 @@ from ._lib import DecodeParams, PoolDesc, TsaError, call, load  # noqa: F401
 
 __all__ = ["KvPool", "DecodeParams", "TsaError", "load", "decode_params", "workspace_bytes",
            "indexer_scores", "topk", "indexer_topk", "sparse_attn_gather", "sparse_decode_attn",
-           "abi_version", "StepGraph"]
+           "abi_version", "StepGraph", "decode_step"]
 
 
 def _i32p(a: Optional[np.ndarray]):
@@ -249,6 +249,15 @@ def sparse_attn_gather(pool, layer, p, q, topk_idx, table_dev, seq_lens, out, wo
     call("tsa_sparse_attn_gather", pool.handle, int(layer), C.byref(p), _ptr(q), _ptr(topk_idx),
          _ptr(table_dev), int(table_dev.shape[-1]), _ptr(seq_lens), _ptr(out), _ptr(workspace),
          _nbytes(workspace), _stream(stream))
+
+
+def decode_step(pool, layer, p, k_new, v_new, idx_new, q, qidx, widx, table_dev, seq_lens, out,
+                workspace, topk_out=None, bad=None, stream=None):
+    """The decode step with each request's new token written at position seq_len - 1 first
+    (fused into the scoring launch where the pool allows; see tsa_decode_step)."""
+    call("tsa_decode_step", pool.handle, int(layer), C.byref(p), _ptr(k_new), _ptr(v_new), _ptr(idx_new),
+         _ptr(bad), _ptr(q), _ptr(qidx), _ptr(widx), _ptr(table_dev), int(table_dev.shape[-1]),
+         _ptr(seq_lens), _ptr(out), _ptr(topk_out), _ptr(workspace), _nbytes(workspace), _stream(stream))
 
 
 class StepGraph:

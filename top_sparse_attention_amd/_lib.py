@@ -59,6 +59,8 @@ SIGNATURES = {
     "tsa_sparse_attn_gather": (i32, [vp, i32, C.POINTER(DecodeParams), vp, vp, vp, i32, vp, vp, vp, sz, vp]),
     "tsa_sparse_decode_attn": (i32, [vp, i32, C.POINTER(DecodeParams), vp, vp, vp, vp, i32, vp, vp, vp,
                                      vp, sz, vp]),
+    "tsa_decode_step": (i32, [vp, i32, C.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                              vp, vp, vp, sz, vp]),
     "tsa_step_graph_create": (i32, [vp, i32, C.POINTER(DecodeParams), C.POINTER(AppendArgs), vp, vp, vp,
                                     vp, i32, vp, vp, vp, vp, sz, C.POINTER(vp)]),
     "tsa_step_graph_launch": (i32, [vp, vp]),

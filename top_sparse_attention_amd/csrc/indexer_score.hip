@@ -180,6 +180,79 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
+// The decode step's own token: request b's new rows land at position seq_len[b] - 1, through the
+// page table like kv_append's.  Fused into the scoring launch, the token's score is taken from its
+// new indexer row directly and the scoring workgroups stop one position short, so no workgroup
+// reads a row the launch writes.
+struct AppendLast {
+    const uint4* k_src;        // [B] rows of num_kv_heads * head_dim_k bf16
+    const uint4* v_src;        // [B] value rows, or null when values alias keys
+    const uint4* i_src;        // [B] indexer rows
+    uint4* k_pool;             // layer bases
+    uint4* v_pool;
+    uint4* i_pool;
+    int k16, v16, i16;         // 16-byte vectors per row
+    int32_t* bad;              // nullable count of tokens whose page-table entry is not a page
+};
+
+__device__ inline float wave_sum_f(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+// one wave per request b (strided over the waves of the caller's grid); with `score`, also
+// writes the token's indexer score (-inf when its page is not valid)
+__device__ void append_last(const AppendLast& f, int wave_id, int n_waves, int batch,
+                            const int32_t* __restrict__ page_table, int max_pages, int page_size,
+                            int num_pages, const int32_t* __restrict__ seq_lens, int max_len,
+                            bool score, const uint16_t* __restrict__ qidx,
+                            const float* __restrict__ widx, int H, int D, float* __restrict__ scores,
+                            int ld) {
+    const int lane = threadIdx.x & 63;
+    for (int b = wave_id; b < batch; b += n_waves) {
+        int len = seq_lens[b];
+        len = len < 0 ? 0 : (len > max_len ? max_len : len);
+        if (len == 0) continue;
+        const int t = len - 1;
+        const int page = page_table[int64_t(b) * max_pages + t / page_size];
+        const bool ok = page >= 0 && page < num_pages;
+        if (ok) {
+            const int64_t slot = int64_t(page) * page_size + t % page_size;
+            for (int i = lane; i < f.k16; i += 64) f.k_pool[slot * f.k16 + i] = f.k_src[int64_t(b) * f.k16 + i];
+            if (f.v_src)
+                for (int i = lane; i < f.v16; i += 64) f.v_pool[slot * f.v16 + i] = f.v_src[int64_t(b) * f.v16 + i];
+            for (int i = lane; i < f.i16; i += 64) f.i_pool[slot * f.i16 + i] = f.i_src[int64_t(b) * f.i16 + i];
+        } else if (lane == 0 && f.bad) {
+            atomicAdd(f.bad, 1);
+        }
+        if (!score) continue;
+        float sc = -INFINITY;
+        if (ok) {
+            const uint16_t* kn = reinterpret_cast<const uint16_t*>(f.i_src + int64_t(b) * f.i16);
+            sc = 0.f;
+            for (int h = 0; h < H; ++h) {
+                const uint16_t* qh = qidx + (int64_t(b) * H + h) * D;
+                float d = 0.f;
+                for (int e = lane; e < D; e += 64)
+                    d = fmaf(__uint_as_float(uint32_t(qh[e]) << 16), __uint_as_float(uint32_t(kn[e]) << 16), d);
+                d = wave_sum_f(d);
+                sc = fmaf(widx[h], fmaxf(d, 0.f), sc);
+            }
+        }
+        if (lane == 0) scores[int64_t(b) * ld + t] = sc;
+    }
+}
+
+__global__ void __launch_bounds__(256) append_last_kernel(AppendLast f, int batch,
+                                                          const int32_t* __restrict__ page_table,
+                                                          int max_pages, int page_size, int num_pages,
+                                                          const int32_t* __restrict__ seq_lens,
+                                                          int max_len) {
+    append_last(f, blockIdx.x * 4 + (threadIdx.x >> 6), gridDim.x * 4, batch, page_table, max_pages,
+                page_size, num_pages, seq_lens, max_len, false, nullptr, nullptr, 0, 0, nullptr, 0);
+}
+
 // ALIGNED: page_size is a power of two and a multiple of the 16-token slot, so every slot lies in
 // one page and the page id is the same for the whole wave.
 //
@@ -197,17 +270,25 @@ __global__ void __launch_bounds__(256) indexer_score_lds_kernel(
     const uint16_t* __restrict__ qidx, const float* __restrict__ widx, int H,
     const int32_t* __restrict__ page_table, int max_pages, int page_size, int page_shift,
     int num_pages, const int32_t* __restrict__ seq_lens, int max_len,
-    const uint16_t* __restrict__ kpool, float* __restrict__ scores, int ld, int tok_per_wave) {
+    const uint16_t* __restrict__ kpool, float* __restrict__ scores, int ld, int tok_per_wave,
+    int batch, AppendLast fused) {
     using G = IdxGeo<D>;
     __shared__ __align__(16) unsigned char ring[4][kRing][G::kSlotBytes];
     __shared__ int32_t wpages[4][kPagesPerWave];   // page ids of each wave's token run
+    const bool append = fused.k_src != nullptr;
+    if (append && int(blockIdx.y) == batch) {     // the extra row of workgroups: the new tokens
+        append_last(fused, blockIdx.x * 4 + (threadIdx.x >> 6), gridDim.x * 4, batch, page_table,
+                    max_pages, page_size, num_pages, seq_lens, max_len, true, qidx, widx,
+                    NB == 0 ? 1 : H, D, scores, ld);
+        return;
+    }
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j16 = lane & 15, g16 = lane >> 4;
     int len = seq_lens[b];
     len = len < 0 ? 0 : (len > max_len ? max_len : len);
     const int t0 = (blockIdx.x * 4 + wave) * tok_per_wave;
-    const int t1 = min(t0 + tok_per_wave, len);
+    const int t1 = min(t0 + tok_per_wave, append ? len - 1 : len);   // the new token is scored above
     if (t0 >= t1) return;
     const int n_units = (t1 - t0 + kUnit - 1) / kUnit;
     const int32_t* pt = page_table + int64_t(b) * max_pages;
@@ -352,24 +433,26 @@ template <int D, int NB>
 hipError_t launch_lds(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                       const void* qidx, const float* widx, const int32_t* page_table,
                       int max_pages, const int32_t* seq_lens, float* scores, int ld,
-                      hipStream_t s, int shift) {
+                      hipStream_t s, int shift, const AppendLast& fused) {
     const tsa_pool_desc& d = pool.d;
     // about 2048 waves over the whole batch (8 per CU), at least a few slots each
     const int64_t total = int64_t(p.batch) * p.max_len;
     int tpw = int((total + 2047) / 2048);
     tpw = std::max(kUnit * 4, std::min(tpw, kMaxTpw));
     tpw = (tpw + kUnit - 1) / kUnit * kUnit;
-    dim3 grid((p.max_len + 4 * tpw - 1) / (4 * tpw), p.batch);
+    dim3 grid((p.max_len + 4 * tpw - 1) / (4 * tpw), p.batch + (fused.k_src ? 1 : 0));
     const uint16_t* kpool = static_cast<const uint16_t*>(pool.idx) + int64_t(layer) * pool.slots() * D;
     const bool aligned = shift >= 0 && d.page_size % kUnit == 0;
     if (aligned)
         hipLaunchKernelGGL((indexer_score_lds_kernel<D, true, NB>), grid, dim3(256), 0, s,
                            static_cast<const uint16_t*>(qidx), widx, p.index_heads, page_table, max_pages,
-                           d.page_size, shift, d.num_pages, seq_lens, p.max_len, kpool, scores, ld, tpw);
+                           d.page_size, shift, d.num_pages, seq_lens, p.max_len, kpool, scores, ld, tpw,
+                           p.batch, fused);
     else
         hipLaunchKernelGGL((indexer_score_lds_kernel<D, false, NB>), grid, dim3(256), 0, s,
                            static_cast<const uint16_t*>(qidx), widx, p.index_heads, page_table, max_pages,
-                           d.page_size, shift, d.num_pages, seq_lens, p.max_len, kpool, scores, ld, tpw);
+                           d.page_size, shift, d.num_pages, seq_lens, p.max_len, kpool, scores, ld, tpw,
+                           p.batch, fused);
     return hipGetLastError();
 }
 
@@ -377,12 +460,12 @@ template <int D>
 hipError_t launch_lds_heads(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                             const void* qidx, const float* widx, const int32_t* page_table,
                             int max_pages, const int32_t* seq_lens, float* scores, int ld,
-                            hipStream_t s, int shift) {
+                            hipStream_t s, int shift, const AppendLast& f) {
     const int h = p.index_heads;
-    if (h == 1) return launch_lds<D, 0>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
-    if (h <= 16) return launch_lds<D, 1>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
-    if (h <= 32) return launch_lds<D, 2>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
-    if (h <= tsa::kMaxIndexHeads) return launch_lds<D, 4>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
+    if (h == 1) return launch_lds<D, 0>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift, f);
+    if (h <= 16) return launch_lds<D, 1>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift, f);
+    if (h <= 32) return launch_lds<D, 2>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift, f);
+    if (h <= tsa::kMaxIndexHeads) return launch_lds<D, 4>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift, f);
     return hipErrorInvalidValue;
 }
 
@@ -438,10 +521,42 @@ bool indexer_supported(const tsa_kv_pool& pool, const tsa_decode_params& p, std:
     return true;
 }
 
+static AppendLast append_args(const tsa_kv_pool& pool, int layer, const NewRows* rows) {
+    AppendLast f{};
+    if (!rows) return f;
+    const tsa_pool_desc& d = pool.d;
+    const int64_t slot0 = int64_t(layer) * pool.slots();
+    f.k16 = d.num_kv_heads * d.head_dim_k * 2 / 16;
+    f.v16 = d.num_kv_heads * d.head_dim_v * 2 / 16;
+    f.i16 = d.index_dim * 2 / 16;
+    f.k_src = static_cast<const uint4*>(rows->k);
+    f.v_src = static_cast<const uint4*>(rows->v);
+    f.i_src = static_cast<const uint4*>(rows->idx);
+    f.k_pool = static_cast<uint4*>(pool.k) + slot0 * f.k16;
+    f.v_pool = pool.v ? static_cast<uint4*>(pool.v) + slot0 * f.v16 : nullptr;
+    f.i_pool = static_cast<uint4*>(pool.idx) + slot0 * f.i16;
+    f.bad = rows->bad;
+    return f;
+}
+
+bool indexer_fuses_append(const tsa_kv_pool& pool) { return lds_kernel_takes(pool); }
+
+hipError_t launch_append_last(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
+                              const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                              const NewRows& rows, hipStream_t s) {
+    const AppendLast f = append_args(pool, layer, &rows);
+    const int grid = int(std::max<int64_t>(1, ceil_div(p.batch, 4)));
+    hipLaunchKernelGGL(append_last_kernel, dim3(grid), dim3(256), 0, s, f, p.batch, page_table,
+                       max_pages, pool.d.page_size, pool.d.num_pages, seq_lens, p.max_len);
+    return hipGetLastError();
+}
+
 hipError_t launch_indexer_scores(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                                  const void* qidx, const float* widx, const int32_t* page_table,
                                  int max_pages, const int32_t* seq_lens, float* scores, int ld,
-                                 hipStream_t s) {
+                                 hipStream_t s, const NewRows* fused) {
+    if (fused && !lds_kernel_takes(pool)) return hipErrorInvalidValue;
+    const AppendLast f = append_args(pool, layer, fused);
     if (lds_kernel_takes(pool)) {
         int shift = -1;
         if ((pool.d.page_size & (pool.d.page_size - 1)) == 0) {
@@ -449,10 +564,10 @@ hipError_t launch_indexer_scores(const tsa_kv_pool& pool, int layer, const tsa_d
             while ((1 << shift) < pool.d.page_size) ++shift;
         }
         switch (pool.d.index_dim) {
-            case 32: return launch_lds_heads<32>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
-            case 64: return launch_lds_heads<64>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
-            case 128: return launch_lds_heads<128>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
-            case 256: return launch_lds_heads<256>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift);
+            case 32: return launch_lds_heads<32>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift, f);
+            case 64: return launch_lds_heads<64>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift, f);
+            case 128: return launch_lds_heads<128>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift, f);
+            case 256: return launch_lds_heads<256>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift, f);
             default: break;
         }
     }

@@ -56,10 +56,24 @@ hipError_t launch_kv_append(const tsa_kv_pool& pool, int layer, int n_tok, const
 constexpr int kMaxIndexHeads = 64;
 // Whether the indexer kernels take this pool / head count (reason in *why when not).
 bool indexer_supported(const tsa_kv_pool& pool, const tsa_decode_params& p, std::string* why);
+// The decode step's new token of every request: rows [B][...] for position seq_len - 1.
+struct NewRows {
+    const void* k = nullptr;
+    const void* v = nullptr;      // null when values alias keys
+    const void* idx = nullptr;
+    int32_t* bad = nullptr;       // nullable count of tokens whose page is not valid
+};
+// With `fused`, the scoring launch also writes the new rows and scores them from the new indexer
+// rows (only where indexer_fuses_append holds).
 hipError_t launch_indexer_scores(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                                  const void* qidx, const float* widx, const int32_t* page_table,
                                  int max_pages, const int32_t* seq_lens, float* scores, int ld,
-                                 hipStream_t s);
+                                 hipStream_t s, const NewRows* fused = nullptr);
+bool indexer_fuses_append(const tsa_kv_pool& pool);
+// The new rows alone (no scores), for the shapes the fused launch does not take.
+hipError_t launch_append_last(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
+                              const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                              const NewRows& rows, hipStream_t s);
 
 // Whether the top-k kernel handles this maximum length.
 bool topk_supported(int max_len);

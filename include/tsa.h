@@ -225,9 +225,9 @@ tsa_status tsa_sparse_decode_attn(tsa_kv_pool* pool, int32_t layer, const tsa_de
  * [B][index_dim], all bf16) are written at position seq_lens[b] - 1 (the token being decoded,
  * already counted in its length) of every request with seq_lens[b] >= 1; then scores, top-k and
  * attention run as in tsa_sparse_decode_attn, the new token included.  Paged-KV page, section
- * "Phân trang": the position's page comes from the page table.  Where pages hold at least 16
- * tokens and index_dim is 32..256, the writes ride in the scoring launch (the new token is
- * scored from its new row); elsewhere a separate launch writes them first.  A token whose
+ * "Phân trang": the position's page comes from the page table.  With one indexer head, pages of
+ * at least 16 tokens and index_dim 32..256, the writes ride in the scoring launch (the new token
+ * is scored from its new row); elsewhere a separate launch writes them first.  A token whose
  * page-table entry is not a page of the pool is not written, scores -inf and is counted in
  * bad_dev (nullable, int32, accumulated).  Other arguments and errors as tsa_sparse_decode_attn. */
 tsa_status tsa_decode_step(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,

@@ -1,6 +1,6 @@
 """tsa_decode_step: the decode step with each request's new token written at position seq_len - 1
-inside the step (fused into the scoring launch where the pool allows, a separate launch
-elsewhere).  Its outputs must equal the separate calls (kv_append, then the whole step) bit for
+inside the step (fused into the scoring launch for one-head indexers on the streaming kernel, a
+separate launch for several heads or small pages).  Its outputs must equal the separate calls (kv_append, then the whole step) bit for
 bit, and the oracle's within the attention bar; a token whose page is missing is counted and
 not written.
 """
@@ -52,6 +52,7 @@ def _scramble_last(st):
 
 @pytest.mark.parametrize("name,kw", [("tiny_b5", {}), ("gqa_b32_8k", {"batch": 6}),
                                      ("mla_b64_32k", {"batch": 3}),
+                                     ("gqa_b32_8k", {"batch": 4, "index_heads": 16}),
                                      ("gqa_b32_8k", {"lens": np.array([1, 9, 300, 2000], np.int32), "page_size": 8})])
 def test_decode_step_equals_separate_calls(tsa, name, kw):
     st = _stage(name, **kw)

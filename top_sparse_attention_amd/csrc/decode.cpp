@@ -222,7 +222,7 @@ tsa_status tsa_decode_step(tsa_kv_pool* pool, int32_t layer, const tsa_decode_pa
     rows.v = v_new_dev;
     rows.idx = idx_new_dev;
     rows.bad = bad_dev;
-    const bool fused = tsa::indexer_fuses_append(*pool);
+    const bool fused = tsa::indexer_fuses_append(*pool, *p);
     hipError_t e = hipSuccess;
     if (!fused) e = tsa::launch_append_last(*pool, layer, *p, page_table_dev, max_pages, seq_lens_dev, rows, s);
     if (e == hipSuccess)

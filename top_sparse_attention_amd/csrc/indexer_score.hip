@@ -227,20 +227,26 @@ __device__ void append_last(const AppendLast& f, int wave_id, int n_waves, int b
             atomicAdd(f.bad, 1);
         }
         if (!score) continue;
-        float sc = -INFINITY;
-        if (ok) {
-            const uint16_t* kn = reinterpret_cast<const uint16_t*>(f.i_src + int64_t(b) * f.i16);
-            sc = 0.f;
-            for (int h = 0; h < H; ++h) {
-                const uint16_t* qh = qidx + (int64_t(b) * H + h) * D;
-                float d = 0.f;
-                for (int e = lane; e < D; e += 64)
-                    d = fmaf(__uint_as_float(uint32_t(qh[e]) << 16), __uint_as_float(uint32_t(kn[e]) << 16), d);
-                d = wave_sum_f(d);
-                sc = fmaf(widx[h], fmaxf(d, 0.f), sc);
+        // lane h dots head h's query with the new key (every lane reads the same key chunks),
+        // then the weighted ReLU terms are summed over the lanes
+        float term = 0.f;
+        if (ok && lane < H) {
+            const uint4* kn = f.i_src + int64_t(b) * f.i16;
+            const uint4* qh = reinterpret_cast<const uint4*>(qidx + (int64_t(b) * H + lane) * D);
+            float d = 0.f;
+            for (int c = 0; c < f.i16; ++c) {
+                const uint4 x = qh[c], y = kn[c];
+                const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    d = fmaf(__uint_as_float(xs[e] << 16), __uint_as_float(ys[e] << 16), d);
+                    d = fmaf(__uint_as_float(xs[e] & 0xffff0000u), __uint_as_float(ys[e] & 0xffff0000u), d);
+                }
             }
+            term = widx[lane] * fmaxf(d, 0.f);
         }
-        if (lane == 0) scores[int64_t(b) * ld + t] = sc;
+        const float sc = wave_sum_f(term);
+        if (lane == 0) scores[int64_t(b) * ld + t] = ok ? sc : -INFINITY;
     }
 }
 
@@ -276,13 +282,13 @@ __global__ void __launch_bounds__(256) indexer_score_lds_kernel(
     __shared__ __align__(16) unsigned char ring[4][kRing][G::kSlotBytes];
     __shared__ int32_t wpages[4][kPagesPerWave];   // page ids of each wave's token run
     const bool append = fused.k_src != nullptr;
-    if (append && int(blockIdx.y) == batch) {     // the extra row of workgroups: the new tokens
+    if (append && blockIdx.y == 0) {     // the first row of workgroups (dispatched first): the new tokens
         append_last(fused, blockIdx.x * 4 + (threadIdx.x >> 6), gridDim.x * 4, batch, page_table,
                     max_pages, page_size, num_pages, seq_lens, max_len, true, qidx, widx,
                     NB == 0 ? 1 : H, D, scores, ld);
         return;
     }
-    const int b = blockIdx.y;
+    const int b = blockIdx.y - (append ? 1 : 0);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j16 = lane & 15, g16 = lane >> 4;
     int len = seq_lens[b];
@@ -539,7 +545,13 @@ static AppendLast append_args(const tsa_kv_pool& pool, int layer, const NewRows*
     return f;
 }
 
-bool indexer_fuses_append(const tsa_kv_pool& pool) { return lds_kernel_takes(pool); }
+// The fused writes take one extra row of workgroups, which pushes as many scoring workgroups into
+// a second round of the grid; they start once the first new-token workgroups are done.  With one
+// head that costs less than the separate launch it replaces (64 x 32k: 162.1 against 165.3 us
+// per step); with 64 heads, whose per-token score takes longer, it lost (194 against 175 us).
+bool indexer_fuses_append(const tsa_kv_pool& pool, const tsa_decode_params& p) {
+    return lds_kernel_takes(pool) && p.index_heads == 1;
+}
 
 hipError_t launch_append_last(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                               const int32_t* page_table, int max_pages, const int32_t* seq_lens,
@@ -555,7 +567,7 @@ hipError_t launch_indexer_scores(const tsa_kv_pool& pool, int layer, const tsa_d
                                  const void* qidx, const float* widx, const int32_t* page_table,
                                  int max_pages, const int32_t* seq_lens, float* scores, int ld,
                                  hipStream_t s, const NewRows* fused) {
-    if (fused && !lds_kernel_takes(pool)) return hipErrorInvalidValue;
+    if (fused && !indexer_fuses_append(pool, p)) return hipErrorInvalidValue;
     const AppendLast f = append_args(pool, layer, fused);
     if (lds_kernel_takes(pool)) {
         int shift = -1;

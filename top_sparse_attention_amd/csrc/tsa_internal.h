@@ -69,7 +69,7 @@ hipError_t launch_indexer_scores(const tsa_kv_pool& pool, int layer, const tsa_d
                                  const void* qidx, const float* widx, const int32_t* page_table,
                                  int max_pages, const int32_t* seq_lens, float* scores, int ld,
                                  hipStream_t s, const NewRows* fused = nullptr);
-bool indexer_fuses_append(const tsa_kv_pool& pool);
+bool indexer_fuses_append(const tsa_kv_pool& pool, const tsa_decode_params& p);
 // The new rows alone (no scores), for the shapes the fused launch does not take.
 hipError_t launch_append_last(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                               const int32_t* page_table, int max_pages, const int32_t* seq_lens,

@@ -229,13 +229,36 @@ tsa_status tsa_sparse_decode_attn(tsa_kv_pool* pool, int32_t layer, const tsa_de
  * at least 16 tokens and index_dim 32..256, the writes ride in the scoring launch (the new token
  * is scored from its new row); elsewhere a separate launch writes them first.  A token whose
  * page-table entry is not a page of the pool is not written, scores -inf and is counted in
- * bad_dev (nullable, int32, accumulated).  Other arguments and errors as tsa_sparse_decode_attn. */
+ * bad_dev (nullable, int32, accumulated).  When max_len <= 1024, min(top_k, max_len) x
+ * num_kv_heads <= 128 and tsa_decode_step_fused takes the shapes, the step runs as
+ * tsa_decode_step_fused (one launch; the workspace is then unused).
+ * Other arguments and errors as tsa_sparse_decode_attn. */
 tsa_status tsa_decode_step(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
                            const void* k_new_dev, const void* v_new_dev, const void* idx_new_dev,
                            int32_t* bad_dev, const void* q_dev, const void* qidx_dev,
                            const float* widx_dev, const int32_t* page_table_dev, int32_t max_pages,
                            const int32_t* seq_lens_dev, float* out_dev, int32_t* topk_dev,
                            void* workspace, size_t ws_bytes, void* stream);
+
+/* tsa_decode_step as one launch: workgroup b runs request b's whole step (write its new token,
+ * score every cached token, select the top k, attend over them), with the scores and the
+ * selection kept on chip.  GLM5.3 page, TileRT paragraph: decode built as one persistent kernel
+ * removes the gaps between its stages; paragraph on serving-engine decode (the GLM-5.2 studies):
+ * small decode steps are dominated by launch overhead.  Results equal tsa_decode_step's (the
+ * same top-k sets; attention within fp32 rounding).  Needs no workspace.  Each request's new
+ * position must lie in a page no other request of the batch maps (tsa_kv_append_check verifies
+ * this), since other workgroups may read the pages they share while it is written.  Limits:
+ * index_dim 8 x a power of two <= 256, index_heads 1..8, head dims multiples of 8, (q heads per
+ * KV head) x head_dim_v <= 2048, and the scores of max_len tokens, min(top_k, max_len) selected
+ * positions and the attention tiles within 64 KiB of LDS (at top_k 2048, max_len up to about
+ * 13,000 tokens);
+ * otherwise TSA_ERR_UNSUPPORTED.  Other arguments and errors as tsa_decode_step. */
+tsa_status tsa_decode_step_fused(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                                 const void* k_new_dev, const void* v_new_dev, const void* idx_new_dev,
+                                 int32_t* bad_dev, const void* q_dev, const void* qidx_dev,
+                                 const float* widx_dev, const int32_t* page_table_dev,
+                                 int32_t max_pages, const int32_t* seq_lens_dev, float* out_dev,
+                                 int32_t* topk_dev, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Captured step.  GLM5.3 page, paragraph on serving-engine prefill and decode (the GLM-5.2

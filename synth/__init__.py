@@ -198,9 +198,12 @@ def index_inputs(w: Workload, seed: int, heads: int, batch: Optional[int] = None
     return q, _weights(_rng(seed, w, _S_WIDX, heads), heads)
 
 
-def queries(w: Workload, seed: int = 0) -> np.ndarray:
-    """Attention queries, bf16 bits [batch, num_q_heads, head_dim_k], N(0, q_std)."""
-    x = _rng(seed, w, _S_Q).standard_normal((w.batch, w.num_q_heads, w.head_dim_k), dtype=np.float32)
+def queries(w: Workload, seed: int = 0, batch: Optional[int] = None) -> np.ndarray:
+    """Attention queries, bf16 bits [batch, num_q_heads, head_dim_k], N(0, q_std); ``batch``
+    defaults to the workload's.  The rows are drawn in order, so a smaller batch is a prefix of
+    a larger one."""
+    n = w.batch if batch is None else int(batch)
+    x = _rng(seed, w, _S_Q).standard_normal((n, w.num_q_heads, w.head_dim_k), dtype=np.float32)
     return f32_to_bf16_bits(x * np.float32(w.q_std))
 
 

@@ -69,3 +69,13 @@ def test_multihead_indexer_inputs():
     q3, w3 = synth.index_inputs(synth.get("gqa_b32_8k"), 0, 17, 40)
     assert q3.shape == (40, 17, 64) and w3.shape == (17,)
     assert np.array_equal(synth.index_weights(synth.get("gqa_b32_8k")), [1.0])
+
+
+def test_queries_of_a_larger_batch_extend_the_default_draw():
+    """Staging more requests than a workload lists draws more query rows; the first rows stay."""
+    w = synth.get("gqa_b32_8k")
+    q = synth.queries(w, 0)
+    q2 = synth.queries(w, 0, 3 * w.batch)
+    assert q2.shape == (3 * w.batch, w.num_q_heads, w.head_dim_k)
+    assert np.array_equal(q2[:w.batch], q)
+    assert np.array_equal(synth.queries(w, 0, 5), q[:5])

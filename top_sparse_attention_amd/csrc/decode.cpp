@@ -214,14 +214,19 @@ tsa_status tsa_decode_step(tsa_kv_pool* pool, int32_t layer, const tsa_decode_pa
     if ((st = check_ws(workspace, ws_bytes, w.total))) return st;
     if (p->batch == 0) return TSA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    float* scores = reinterpret_cast<float*>(at(workspace, w.scores));
-    int32_t* topk = topk_dev ? topk_dev : reinterpret_cast<int32_t*>(at(workspace, w.topk));
-    const int ld = scores_ld(p->max_len);
     tsa::NewRows rows;
     rows.k = k_new_dev;
     rows.v = v_new_dev;
     rows.idx = idx_new_dev;
     rows.bad = bad_dev;
+    if (tsa::fused_step_preferred(*pool, *p))
+        return tsa::hip_check(tsa::launch_fused_step(*pool, layer, *p, rows, q_dev, qidx_dev, widx_dev,
+                                                     page_table_dev, max_pages, seq_lens_dev, out_dev,
+                                                     topk_dev, s),
+                              "one-launch step");
+    float* scores = reinterpret_cast<float*>(at(workspace, w.scores));
+    int32_t* topk = topk_dev ? topk_dev : reinterpret_cast<int32_t*>(at(workspace, w.topk));
+    const int ld = scores_ld(p->max_len);
     const bool fused = tsa::indexer_fuses_append(*pool, *p);
     hipError_t e = hipSuccess;
     if (!fused) e = tsa::launch_append_last(*pool, layer, *p, page_table_dev, max_pages, seq_lens_dev, rows, s);
@@ -235,6 +240,33 @@ tsa_status tsa_decode_step(tsa_kv_pool* pool, int32_t layer, const tsa_decode_pa
                                   seq_lens_dev, out_dev,
                                   plan.partial_bytes ? at(workspace, w.partial) : nullptr, s);
     return tsa::hip_check(e, "decode step launch");
+}
+
+tsa_status tsa_decode_step_fused(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                                 const void* k_new_dev, const void* v_new_dev, const void* idx_new_dev,
+                                 int32_t* bad_dev, const void* q_dev, const void* qidx_dev,
+                                 const float* widx_dev, const int32_t* page_table_dev,
+                                 int32_t max_pages, const int32_t* seq_lens_dev, float* out_dev,
+                                 int32_t* topk_dev, void* stream) {
+    tsa_status st = check_common(pool, layer, p, page_table_dev, max_pages, seq_lens_dev);
+    if (st) return st;
+    if ((st = check_indexer(pool, p, qidx_dev, widx_dev))) return st;
+    if ((st = check_attn(pool, p, q_dev, out_dev))) return st;
+    std::string why;
+    if (!tsa::fused_step_supported(*pool, *p, &why)) return fail(TSA_ERR_UNSUPPORTED, why);
+    if (p->batch > 0 && (!k_new_dev || !idx_new_dev)) return fail(TSA_ERR_INVALID, "NULL new key or indexer rows");
+    if (pool->d.v_from_k ? v_new_dev != nullptr : (p->batch > 0 && v_new_dev == nullptr))
+        return fail(TSA_ERR_INVALID, "v_new must be NULL exactly when the pool has v_from_k");
+    if (p->batch == 0) return TSA_OK;
+    tsa::NewRows rows;
+    rows.k = k_new_dev;
+    rows.v = v_new_dev;
+    rows.idx = idx_new_dev;
+    rows.bad = bad_dev;
+    return tsa::hip_check(tsa::launch_fused_step(*pool, layer, *p, rows, q_dev, qidx_dev, widx_dev,
+                                                 page_table_dev, max_pages, seq_lens_dev, out_dev,
+                                                 topk_dev, static_cast<hipStream_t>(stream)),
+                          "one-launch step");
 }
 
 }  // extern "C"

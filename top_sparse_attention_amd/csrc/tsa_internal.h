@@ -103,6 +103,17 @@ hipError_t launch_attention_gqa(const tsa_kv_pool& pool, int layer, const tsa_de
                                 const AttnPlan& plan, const void* q, const int32_t* topk,
                                 const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                                 float* out, float* part_ml, float* part_acc, hipStream_t s);
+// The whole step of each request in one workgroup, one launch (short contexts).
+bool fused_step_supported(const tsa_kv_pool& pool, const tsa_decode_params& p, std::string* why);
+// tsa_decode_step takes the one-launch step by itself up to this max_len and this many selected
+// (row, KV head) pairs per request, min(top_k, max_len) * num_kv_heads.
+constexpr int kFusedAutoMaxLen = 1024;
+constexpr int kFusedAutoRows = 128;
+bool fused_step_preferred(const tsa_kv_pool& pool, const tsa_decode_params& p);
+hipError_t launch_fused_step(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
+                             const NewRows& rows, const void* q, const void* qidx, const float* widx,
+                             const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                             float* out, int32_t* topk, hipStream_t s);
 hipError_t launch_attention(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                             const AttnPlan& plan, const void* q, const int32_t* topk,
                             const int32_t* page_table, int max_pages, const int32_t* seq_lens,

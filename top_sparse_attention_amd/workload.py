@@ -85,7 +85,8 @@ def stage(w, seed: int = 0, batch: Optional[int] = None, lens: Optional[np.ndarr
     H_I = w.index_heads if index_heads is None else int(index_heads)
 
     qidx_np, widx_np = synth.index_inputs(w, seed, H_I, B)
-    q_np = synth.queries(w, seed)[:B]
+    q_np = synth.queries(w, seed, B)
+    assert q_np.shape[0] == B and qidx_np.shape[0] == B
 
     table_dev = _dev(table, device)
     lens_dev = _dev(lens, device)

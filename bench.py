@@ -264,6 +264,77 @@ def bench_mla_modes(args):
                       "mha_faster_at": faster, "points": points}), flush=True)
 
 
+def bench_one_launch(args):
+    """The one-launch step (tsa_decode_step_fused: each request's append, scores, top-k and
+    attention in one workgroup) against the separate launches (kv_append, then scores, top-k and
+    attention) on short-context shapes: the tiny worked example and 32-head / 4-KV-head requests
+    of 256..2048 tokens at several batch sizes and top-k.  Both are timed with HIP events over
+    back-to-back calls; at these sizes host launch time can exceed the kernels', so the kernel
+    durations of record come from a kernel trace of this same run.  Prints one JSON line."""
+    import torch
+    import synth
+    import top_sparse_attention_amd as tsa
+    from top_sparse_attention_amd import workload
+
+    tsa.load()
+    cases = [("tiny_b5", None, None),
+             ("gqa_b32_8k", (32, 256), None),
+             ("gqa_b32_8k", (32, 1024), 64),
+             ("gqa_b32_8k", (32, 1024), 128),
+             ("gqa_b32_8k", (8, 1024), 128),
+             ("gqa_b32_8k", (128, 1024), 64),
+             ("gqa_b32_8k", (256, 512), 64),
+             ("gqa_b32_8k", (32, 2048), 64)]
+    points = []
+    for name, shape, k in cases:
+        kw = {} if shape is None else {"lens": np.full(shape[0], shape[1], np.int32)}
+        st = workload.stage(synth.get(name), seed=args.seed, **kw)
+        if k is not None:
+            st.params.top_k = k          # the staged top-k buffers hold the workload's larger k
+        B = len(st.lens)
+        rows = []
+        for src in (st.new_k, st.new_v, st.new_idx):
+            if src is None:
+                rows.append(None)
+                continue
+            full = torch.zeros((B,) + tuple(src.shape[1:]), dtype=src.dtype, device="cuda")
+            full[st.new_req.long()] = src
+            rows.append(full)
+        kn, vn, inew = rows
+
+        def one_launch():
+            tsa.decode_step_fused(st.pool, 0, st.params, kn, vn, inew, st.q, st.qidx, st.widx,
+                                  st.table_dev, st.lens_dev, st.out, topk_out=st.topk)
+
+        def separate():
+            st.pool.append(0, st.new_req, st.new_pos, st.table_dev, B, st.new_k, st.new_v, st.new_idx)
+            tsa.sparse_decode_attn(st.pool, 0, st.params, st.q, st.qidx, st.widx, st.table_dev,
+                                   st.lens_dev, st.out, st.workspace, topk_out=st.topk)
+
+        pt = {"workload": name, "requests": B, "context": int(st.lens.max()), "top_k": int(st.params.top_k),
+              "kv_heads": st.w.num_kv_heads, "q_heads": st.w.num_q_heads}
+        for label, fn in (("one_launch_us", one_launch), ("separate_us", separate)):
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = 100
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            pt[label] = round(e0.elapsed_time(e1) * 1e3 / n, 2)
+        points.append(pt)
+        print(f"[bench] {name} B={B} L={pt['context']} k={pt['top_k']}: one launch {pt['one_launch_us']} us, "
+              f"separate {pt['separate_us']} us", file=sys.stderr, flush=True)
+        del st
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "decode step, one launch vs separate launches (us per step, HIP events "
+                                "over back-to-back calls)", "unit": "us", "higher_is_better": False,
+                      "dtype": "bf16", "data": "synthetic", "points": points}), flush=True)
+
+
 def bench_tier(args):
     """The tiered workload: per step, every layer plans its pages on the host, fetches the
     misses on a side stream and attends over the HBM cache; prints one JSON line with
@@ -455,6 +526,8 @@ def main():
                     help="cache unit of the tiered workload: whole pages or single token rows")
     ap.add_argument("--mla-modes", action="store_true",
                     help="compare latent attention in MQA mode and MHA mode over context lengths and exit")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="time the one-launch step against the separate launches on short contexts")
     ap.add_argument("--separate", action="store_true",
                     help="time the step as separate calls (kv_append, scores, top-k, attention) "
                          "instead of tsa_decode_step")
@@ -484,6 +557,9 @@ def main():
 
     if args.mla_modes:
         bench_mla_modes(args)
+        return
+    if args.one_launch:
+        bench_one_launch(args)
         return
     if synth.get(args.workload).num_layers > 1:
         bench_tier(args)

@@ -625,6 +625,10 @@ def main():
     # between the kernels.  An interval includes the launch gap before its kernel, so these
     # durations are upper bounds of the kernels' own.
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # the timed loop may have run other kernels (the one-launch step): warm the separate calls up
+    # first, so that no first-launch cost lands in the event pass
+    for _ in range(3):
+        step(None)
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(events[i])

@@ -5,7 +5,7 @@ whole step) bit for bit, and the oracle's; attention within fp32 rounding of the
 and within 2e-3 of the oracle.  Cases: the tiny worked example, ragged lengths with 8-token
 pages (contexts shorter than top_k, a 1-token context, several tiles), several indexer heads,
 one query head per KV head with 192/128 dims (the MHA mode of latent attention), dense and
-sparse requests in one batch, and a missing page.
+sparse requests in one batch, the latent layout with aliased values, and a missing page.
 """
 import numpy as np
 import pytest
@@ -66,9 +66,20 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("name,kw", CASES)
+@pytest.mark.parametrize("name,kw", CASES + [
+    # the latent layout (values are the first 512 dims of the 576-dim key row) with 4 query heads:
+    # aliased values, 32-row tiles, and a sparse selection of 2048 out of 5000 positions
+    ("mla_b64_32k", {"q_heads": 4, "lens": np.array([300, 2049, 5000], np.int32)})])
 def test_fused_step_equals_separate_calls_and_oracle(tsa, name, kw):
-    st = _stage(name, **kw)
+    kw = dict(kw)
+    hq = kw.pop("q_heads", None)
+    if hq is None:
+        st = _stage(name, **kw)
+    else:
+        import dataclasses
+        from top_sparse_attention_amd import workload
+        print(f"[stage] {name} q_heads={hq} {kw}", flush=True)
+        st = workload.stage(dataclasses.replace(synth.get(name), num_q_heads=hq), **kw)
     kn, vn, inew = _new_rows(st)
     st.pool.append(0, st.new_req, st.new_pos, st.table_dev, len(st.lens), st.new_k, st.new_v, st.new_idx)
     tsa.sparse_decode_attn(st.pool, 0, st.params, st.q, st.qidx, st.widx, st.table_dev, st.lens_dev,

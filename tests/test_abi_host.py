@@ -45,6 +45,28 @@ def test_exports_every_declared_symbol():
     assert set(_lib.SIGNATURES) >= names
 
 
+def _declared_arity():
+    """Parameter count of every tsa_* function declared in include/*.h."""
+    out = {}
+    for h in os.listdir(os.path.join(ROOT, "include")):
+        if not h.endswith(".h"):
+            continue
+        text = re.sub(r"/\*.*?\*/", " ", open(os.path.join(ROOT, "include", h)).read(), flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?\w+\**\s+\**(tsa_\w+)\s*\(([^)]*)\)\s*;", text, re.M):
+            params = " ".join(m.group(2).split())
+            out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_bindings_match_declared_arity():
+    """Every ctypes signature in the binding has as many arguments as the C declaration."""
+    arity = _declared_arity()
+    assert arity, "no declarations parsed"
+    for name, (_, args) in _lib.SIGNATURES.items():
+        assert name in arity, f"{name} has a binding but no declaration"
+        assert len(args) == arity[name], f"{name}: binding takes {len(args)} arguments, header {arity[name]}"
+
+
 def test_abi_version():
     assert tsa.abi_version() == 1
 

@@ -3,7 +3,7 @@
 Bar: the pool rows it writes and the top-k sets equal the separate calls (kv_append, then the
 whole step) bit for bit, and the oracle's; attention within fp32 rounding of the separate calls
 and within 2e-3 of the oracle.  Cases: the tiny worked example, ragged lengths with 8-token
-pages (contexts shorter than top_k, a 1-token context, several tiles), several indexer heads,
+pages (an empty request, contexts shorter than top_k, a 1-token context, several tiles), several indexer heads,
 one query head per KV head with 192/128 dims (the MHA mode of latent attention), dense and
 sparse requests in one batch, the latent layout with aliased values, and a missing page.
 """
@@ -59,7 +59,7 @@ def _pool_bits(st):
 
 CASES = [
     ("tiny_b5", {}),
-    ("gqa_b32_8k", {"lens": np.array([1, 9, 300, 1000, 777, 513], np.int32), "page_size": 8}),
+    ("gqa_b32_8k", {"lens": np.array([1, 9, 0, 300, 1000, 777, 513], np.int32), "page_size": 8}),
     ("gqa_b32_8k", {"lens": np.array([2048, 4100, 3000], np.int32), "index_heads": 4}),
     ("gqa_b32_8k", {"lens": np.array([700, 64, 65, 5000], np.int32), "index_heads": 8, "page_size": 16}),
     ("mla_mha_b64_4k", {"lens": np.array([100, 257], np.int32)}),
@@ -101,6 +101,8 @@ def test_fused_step_equals_separate_calls_and_oracle(tsa, name, kw):
             assert torch.equal(got, ref), "pool rows differ"
         assert torch.equal(st.topk, ref_t), f"top-k differs (round {rep})"
         assert not torch.isnan(st.out).any()
+        for b in np.nonzero(st.lens == 0)[0]:     # an empty request: zeros and no selection
+            assert not st.out[b].any() and (st.topk[b] == -1).all()
         err = (st.out - ref_o).abs().max().item() / max(ref_o.abs().max().item(), 1e-30)
         assert err < 1e-5, f"attention differs from the separate calls by {err:.3g} (round {rep})"
         if first is None:

@@ -189,6 +189,27 @@ def test_grow():
         paging.grow_page_tables(out["table"], out["num_pages"], [0, 17], 16, out["free"])
 
 
+def test_grow_several_requests_by_hand():
+    """Three requests grown at once, worked by hand from the allocation reading (requests in
+    index order, each one's new logical pages in order, popped from the front of the free
+    list).  Lengths 16 / 17 / 5 at P = 16 hold 1 / 2 / 1 pages: free order 7 3 5 1 0 2 6 4
+    gives request 0 page 7, request 1 pages 3 and 5, request 2 page 1, leaving 0 2 6 4.
+    Growing to 33 / 17 / 40 tokens needs 3 / 2 / 3 pages: request 0 takes 0 and 2, request 1
+    nothing, request 2 takes 6 and 4.  A round-robin or per-page-index order would give
+    request 0 pages 0 and 6 instead."""
+    free = np.array([7, 3, 5, 1, 0, 2, 6, 4])
+    out = paging.build_page_tables([16, 17, 5], 16, free, max_pages=3)
+    assert out["table"].tolist() == [[7, -1, -1], [3, 5, -1], [1, -1, -1]]
+    assert list(out["free"]) == [0, 2, 6, 4]
+    g = paging.grow_page_tables(out["table"], out["num_pages"], [33, 17, 40], 16, out["free"])
+    assert g["table"].tolist() == [[7, 0, 2], [3, 5, -1], [1, 6, 4]]
+    assert g["num_pages"].tolist() == [3, 2, 3] and list(g["free"]) == []
+    # one page more than the pool has left (request 1 to 3 pages): refused, tables unchanged
+    with pytest.raises(MemoryError):
+        paging.grow_page_tables(g["table"], g["num_pages"], [33, 33, 40], 16, g["free"])
+    assert g["table"].tolist() == [[7, 0, 2], [3, 5, -1], [1, 6, 4]]
+
+
 def test_physical_slot():
     out = paging.build_page_tables(LENS, P, np.arange(66)[::-1].copy())
     assert paging.physical_slot(out["table"], 0, 0, P) == 65 * 16

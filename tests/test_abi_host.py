@@ -353,3 +353,20 @@ def test_lru_tier_refuses_fetch_without_device_memory():
     table, _ = tier.plan(0, 0, np.array([[0]], dtype=np.int32))
     with pytest.raises(tsa.TsaError):
         _lib.call("tsa_lru_fetch", tier.handle, 1, None, None, None, 0, None)
+
+
+def test_latent_selection_beyond_64_splits_leaves_the_matrix_core_kernel():
+    """A latent-shape selection longer than 64 row lists of 1,024 tokens would need more splits
+    than the split combine merges; the plan must then take the vector-ALU kernel, whose split
+    count stays <= 64.  Checked through the workspace size (no kernel runs): with 64 splits at
+    most, the partials of 1 request x 64 heads x 512 value dims fit in
+    (2 n + n * 512) * 4 bytes with n = 64 * 64."""
+    pool = tsa.KvPool(1600, 64, 1, 576, 512, v_from_k=True, index_dim=128, allocate=False)
+    L = 100_000
+    p = tsa.decode_params(1, 64, L, L, 1.0 / 24.0)
+    ws = tsa.workspace_bytes(pool, p)
+    scores = -(-L // 64) * 64 * 4
+    topk = -(-(L * 4) // 256) * 256
+    n = 64 * 64
+    partial = (2 * n + n * 512) * 4
+    assert 0 < ws <= scores + topk + partial + 3 * 256

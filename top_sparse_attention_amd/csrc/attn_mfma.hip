@@ -479,7 +479,9 @@ bool mfma_latent_applicable(const tsa_kv_pool& pool, const tsa_decode_params& p)
     if (pool.slots() >= (int64_t(1) << 31)) return false;   // slots kept as 32-bit in LDS
     int splits = 0;
     const int chunk = mfma_latent_chunk(p, &splits);
-    return chunk <= kMaxChunk && mfma_smem<576, 512>(chunk) <= 160 * 1024;
+    // the split combine merges at most 64 splits: a longer selection (more than 64 row lists
+    // of kMaxChunk) goes to the vector-ALU kernel, whose chunks are not bounded by LDS
+    return splits <= 64 && chunk <= kMaxChunk && mfma_smem<576, 512>(chunk) <= 160 * 1024;
 }
 
 int mfma_latent_chunk(const tsa_decode_params& p, int* splits) {

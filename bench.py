@@ -8,10 +8,13 @@ every cached token, top-k selection, attention over the selected tokens (+ split
 Inputs are seeded synthetic data resident in HBM before timing starts.  The default workload
 is 64 requests x 32768 tokens, top-2048, 64 query heads over one 576-dim latent KV head.
 
-Prints ONE JSON line.  `value` = requests decoded per second (one token each) over the timed
-steps.  `roofline` covers the dominant kernel (the indexer score, which streams every cached
-indexer key); `roofline_attention` the gather-attention kernels.  Kernel durations come from
-HIP events recorded on the launch stream around each launch inside the timed region.
+Prints ONE JSON line.  `value` = requests decoded per second (one token each) over K steps run
+back to back; the steps rotate through 8 pre-drawn query sets, so each selects other rows than
+the step before.  `step_ms` gives the median, p10 and p90 of per-step times, warm and with a
+512 MiB scrub before each step.  `roofline` covers the dominant kernel (the indexer score,
+which streams every cached indexer key); `roofline_attention` the gather-attention kernels.
+Kernel durations come from HIP events recorded on the launch stream between the launches of a
+second pass of the same steps.
 """
 from __future__ import annotations
 
@@ -32,11 +35,16 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 
 
 def _src_hash(name: str) -> str:
-    """Hash of a kernel source's code: comment-only lines and blank lines are left out, so that
+    """Hash of what a kernel's machine code depends on: its source, the headers every kernel
+    source includes, and the compiler flags.  Comment-only and blank lines are left out, so that
     editing a comment does not disown the counters taken on the same code."""
-    p = os.path.join(ROOT, "top_sparse_attention_amd", "csrc", name)
-    code = [ln.rstrip() for ln in open(p, encoding="utf-8")
-            if ln.strip() and not ln.lstrip().startswith("//")]
+    csrc = os.path.join(ROOT, "top_sparse_attention_amd", "csrc")
+    code = []
+    for f in (name, "tsa_internal.h", "mfma_lds.h"):
+        code += [ln.rstrip() for ln in open(os.path.join(csrc, f), encoding="utf-8")
+                 if ln.strip() and not ln.lstrip().startswith("//")]
+    from top_sparse_attention_amd import build as _build
+    code.append(" ".join(_build.FLAGS))
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
@@ -63,17 +71,11 @@ def _traffic(kernel_src: str, key: str):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(w, seed: int, budget_s: float = 15.0):
-    """The oracle as it stands, timed on this host on a bounded sample of the same workload:
-    whole requests (scores over every token, full-sort top-k, float64 attention) until the
-    time budget is spent.  Returns requests (= decode tokens) per second."""
+def _oracle_rate(w, seed: int, budget_s: float):
+    """Requests per second of the oracle's whole decode step over whole requests of workload w,
+    until the time budget is spent; returns (rate, sample description)."""
     import synth
     from oracle import decode
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = 1
     lens = synth.lens(w, seed)
     qi = synth.index_queries(w, seed)
     q = synth.queries(w, seed)
@@ -92,11 +94,29 @@ def cpu_baseline(w, seed: int, budget_s: float = 15.0):
             done += 1
         passes = max(passes, reps)
         b += 1
-    return {"value": done / spent, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"{done} request steps over the first {b} of {len(lens)} requests of {w.name} "
-                      f"(full context each, up to {passes} repeats per request), {spent:.1f} s of "
-                      f"oracle time; input generation not timed",
-            "cpu": _cpu_model(), "host_cores": len(os.sched_getaffinity(0))}
+    return done / spent, (f"{done} request steps over the first {b} of {len(lens)} requests of {w.name} "
+                          f"(full context each, up to {passes} repeats per request), {spent:.1f} s of "
+                          f"oracle time; input generation not timed")
+
+
+def cpu_baseline(w, seed: int, budget_s: float = 12.0):
+    """The oracle as it stands, timed on this host on a bounded sample of the same workload
+    (whole requests: scores over every token, full-sort top-k, float64 attention), twice: with
+    the BLAS thread pool limited to one thread, and with every core this process may use.
+    Returns requests (= decode tokens) per second of the all-core run, with the one-thread run
+    beside it."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=1):
+        one, one_sample = _oracle_rate(w, seed, budget_s)
+    with threadpool_limits(limits=cores):
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        allc, all_sample = _oracle_rate(w, seed, budget_s)
+    return {"value": allc, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+            "sample": all_sample, "cpu": _cpu_model(), "host_cores": cores,
+            "one_thread": {"value": one, "cores": 1, "sample": one_sample},
+            "note": "integer scores and the top-k sort are single-threaded numpy; the BLAS thread "
+                    "count changes only the float64 attention"}
 
 
 def _cpu_model() -> str:
@@ -516,7 +536,10 @@ def main():
     ap.add_argument("--workload", default="mla_b64_32k")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle time for each of the two host runs (1 thread, all cores)")
+    ap.add_argument("--query-sets", type=int, default=8,
+                    help="pre-drawn query sets the steps rotate through (different rows per step)")
     ap.add_argument("--tier-requests", type=int, default=16,
                     help="requests of the tiered workload (the full 256 needs 128 GiB of pinned memory)")
     ap.add_argument("--tier-positions", choices=("drawn", "indexer"), default="drawn",
@@ -550,10 +573,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import torch
     import synth
-    import top_sparse_attention_amd as tsa
-    from top_sparse_attention_amd import workload
 
     if args.mla_modes:
         bench_mla_modes(args)
@@ -564,6 +584,22 @@ def main():
     if synth.get(args.workload).num_layers > 1:
         bench_tier(args)
         return
+    bench_step(args)
+
+
+def _pct(xs):
+    xs = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(xs)), 5), "p10": round(float(np.percentile(xs, 10)), 5),
+            "p90": round(float(np.percentile(xs, 90)), 5), "mean": round(float(xs.mean()), 5)}
+
+
+def bench_step(args):
+    """The single-layer decode step (every workload but the tiered one); prints the JSON line."""
+    import torch
+    import synth
+    import top_sparse_attention_amd as tsa
+    from top_sparse_attention_amd import workload
+
     tsa.load()
     w = synth.get(args.workload)
     if args.copy_calib_mib:
@@ -576,65 +612,104 @@ def main():
     stream = torch.cuda.current_stream()
     ld = int(np.ceil(max(st.params.max_len, 1) / 64) * 64)
     scores = torch.empty((B, ld), dtype=torch.float32, device="cuda")
+    H_I = st.params.index_heads
 
-    def step(ev=None):
+    # Query sets: set 0 is the staged one (the parity tests' case); the others are further seeded
+    # draws of the attention and indexer queries, so that consecutive steps select different rows
+    # and no step re-reads the rows the one before it gathered.
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a.view(np.int16))).cuda()
+    qsets = [(st.q, st.qidx)]
+    for i in range(1, max(1, args.query_sets)):
+        qsets.append((dev(synth.queries(w, args.seed + i, B)),
+                      dev(synth.index_inputs(w, args.seed + i, H_I, B)[0])))
+    n_sets = len(qsets)
+
+    def step(i, ev=None):
+        q, qidx = qsets[i % n_sets]
         if ev is not None:
             ev[0].record(stream)
         if st.new_req is not None:
             st.pool.append(0, st.new_req, st.new_pos, st.table_dev, B, st.new_k, st.new_v, st.new_idx)
         if ev is not None:
             ev[1].record(stream)
-        tsa.indexer_scores(st.pool, 0, st.params, st.qidx, st.widx, st.table_dev, st.lens_dev, scores)
+        tsa.indexer_scores(st.pool, 0, st.params, qidx, st.widx, st.table_dev, st.lens_dev, scores)
         if ev is not None:
             ev[2].record(stream)
         tsa.topk(st.params, scores, st.lens_dev, st.topk)
         if ev is not None:
             ev[3].record(stream)
-        tsa.sparse_attn_gather(st.pool, 0, st.params, st.q, st.topk, st.table_dev, st.lens_dev,
+        tsa.sparse_attn_gather(st.pool, 0, st.params, q, st.topk, st.table_dev, st.lens_dev,
                                st.out, st.workspace)
         if ev is not None:
             ev[4].record(stream)
 
-    timed = step
+    timed = lambda i: step(i)
+    launch = "separate calls"
     if st.new_req is not None and len(st.new_req) == B and not args.separate:
         # the library's whole step: the new token of every request written inside the step
         # (tsa_decode_step); the kernel-timing pass below runs the same kernels as separate calls
         k_new, v_new, i_new = st.new_k, st.new_v, st.new_idx
-        timed = lambda: tsa.decode_step(st.pool, 0, st.params, k_new, v_new, i_new, st.q, st.qidx,
-                                        st.widx, st.table_dev, st.lens_dev, st.out, st.workspace,
-                                        topk_out=st.topk, stream=stream)
+        launch = "tsa_decode_step"
+
+        def timed(i):
+            q, qidx = qsets[i % n_sets]
+            tsa.decode_step(st.pool, 0, st.params, k_new, v_new, i_new, q, qidx, st.widx,
+                            st.table_dev, st.lens_dev, st.out, st.workspace, topk_out=st.topk,
+                            stream=stream)
     if args.graph:
-        graph = tsa.StepGraph(st.pool, 0, st.params, st.q, st.qidx, st.widx, st.table_dev, st.lens_dev,
-                              st.out, st.workspace, topk_out=st.topk,
-                              append=None if st.new_req is None else
-                              (st.new_req, st.new_pos, st.new_k, st.new_v, st.new_idx, None))
-        timed = lambda: graph.launch(stream)
-    for _ in range(args.warmup):
-        timed()
+        launch = "graph"
+        graphs = [tsa.StepGraph(st.pool, 0, st.params, q, qidx, st.widx, st.table_dev, st.lens_dev,
+                                st.out, st.workspace, topk_out=st.topk,
+                                append=None if st.new_req is None else
+                                (st.new_req, st.new_pos, st.new_k, st.new_v, st.new_idx, None))
+                  for q, qidx in qsets]
+        timed = lambda i: graphs[i % n_sets].launch(stream)
+    for i in range(args.warmup):
+        timed(i)
     torch.cuda.synchronize()
-    # The throughput pass has no event between kernels: on this runtime each such event adds
-    # a few microseconds of idle time before the next kernel (about 18 us over the 4 inner
-    # events of a step, measured), which would charge the step for its own instrumentation.
+    # Throughput (`value`): K steps back to back, no event between kernels or steps (on this
+    # runtime an event between two kernels leaves the GPU idle for a few microseconds).
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        timed()
+    for i in range(args.steps):
+        timed(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
-    # Per-kernel durations: the same steps again, with HIP events recorded on the launch stream
-    # between the kernels.  An interval includes the launch gap before its kernel, so these
-    # durations are upper bounds of the kernels' own.
+
+    # Step-time distribution: events around each step, back to back ("warm"), then with a
+    # 512 MiB scrub written before each step outside its interval, so that neither L2 nor the
+    # 256 MB last-level cache holds anything of the step before ("scrubbed").
+    scrub = torch.zeros((512 << 20) // 4, dtype=torch.int32, device="cuda")
+    dist = {}
+    for label, do_scrub in (("warm", False), ("scrubbed", True)):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i in range(args.steps):
+            if do_scrub:
+                scrub.add_(1)
+            evs[i][0].record(stream)
+            timed(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        dist[label] = _pct([a.elapsed_time(b_) for a, b_ in evs])
+    del scrub
+
+    # Per-kernel durations: the same steps again as separate calls, with HIP events recorded on
+    # the launch stream between the kernels.  An interval includes the launch gap before its
+    # kernel, so these durations are upper bounds of the kernels' own.
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     # the timed loop may have run other kernels (the one-launch step): warm the separate calls up
     # first, so that no first-launch cost lands in the event pass
-    for _ in range(3):
-        step(None)
+    for i in range(3):
+        step(i)
     torch.cuda.synchronize()
     for i in range(args.steps):
-        step(events[i])
+        step(i, events[i])
     torch.cuda.synchronize()
     per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in events])  # ms
     t_append, t_index, t_topk, t_attn = per.mean(axis=0)
+    # the last step of that pass used query set (K - 1) mod n_sets: its selection is in st.topk
 
     # algorithmic bytes per launch
     lens = st.lens.astype(np.int64)
@@ -696,11 +771,14 @@ def main():
                    "top_k": w.top_k, "page_size": w.page_size, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim_k": w.head_dim_k, "head_dim_v": w.head_dim_v,
                    "index_dim": D_I, "index_heads": w.index_heads, "parallelism": "none",
-                   "launch": "graph" if args.graph else ("separate calls" if args.separate else "tsa_decode_step")},
+                   "launch": launch, "query_sets": n_sets},
+        "step_ms": dict(dist, note="per-step HIP events; 'scrubbed' writes 512 MiB before each step, "
+                                   "outside its interval; 'warm' runs the steps back to back"),
         "kernels_ms": {"kv_append": round(t_append, 5), "indexer_score": round(t_index, 5),
                        "topk": round(t_topk, 5), "attention": round(t_attn, 5)},
         "kernel_timing": "HIP events between kernels on the launch stream, over a second pass of "
-                         "the same steps (the throughput pass has no events between kernels)",
+                         "the same steps as separate calls (the throughput pass has no events "
+                         "between kernels)",
         "roofline": dict(roof(idx_bytes, idx_unique, t_index, "indexer_score.hip", f"indexer_score/{w.name}"),
                          flops=idx_flops, tflops=round(idx_flops / (t_index * 1e-3) / 1e12, 2)),
         "roofline_attention": dict(roof(attn_bytes, attn_unique, t_attn, attn_src, f"attention/{w.name}"),

@@ -240,6 +240,24 @@ tsa_status tsa_decode_step(tsa_kv_pool* pool, int32_t layer, const tsa_decode_pa
                            const int32_t* seq_lens_dev, float* out_dev, int32_t* topk_dev,
                            void* workspace, size_t ws_bytes, void* stream);
 
+/* tsa_decode_step for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same step, arguments and results,
+ * with the workspace taken from a fixed scratch array inside the library instead of a caller
+ * buffer.  Each GPU the library runs on holds one 64 MiB array (256-byte aligned) from the time
+ * the library's code is loaded on it until the process ends; the call allocates nothing and
+ * looks the current device's array up on its first call on that device.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (on different streams, or from different
+ * threads without ordering) race and give wrong results.  The array keeps the last call's
+ * contents, which no call depends on.  Returns TSA_ERR_CAPACITY when the step's workspace
+ * (tsa_sparse_decode_workspace) exceeds 64 MiB; other errors as tsa_decode_step. */
+tsa_status tsa_decode_step_noalloc(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                                   const void* k_new_dev, const void* v_new_dev,
+                                   const void* idx_new_dev, int32_t* bad_dev, const void* q_dev,
+                                   const void* qidx_dev, const float* widx_dev,
+                                   const int32_t* page_table_dev, int32_t max_pages,
+                                   const int32_t* seq_lens_dev, float* out_dev, int32_t* topk_dev,
+                                   void* stream);
+
 /* tsa_decode_step as one launch: workgroup b runs request b's whole step (write its new token,
  * score every cached token, select the top k, attend over them), with the scores and the
  * selection kept on chip.  GLM5.3 page, TileRT paragraph: decode built as one persistent kernel

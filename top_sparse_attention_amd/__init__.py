@@ -22,7 +22,7 @@ from ._lib import DecodeParams, PoolDesc, TsaError, call, load  # noqa: F401
 __all__ = ["KvPool", "DecodeParams", "TsaError", "load", "decode_params", "workspace_bytes",
            "indexer_scores", "topk", "indexer_topk", "sparse_attn_gather", "sparse_decode_attn",
            "abi_version", "StepGraph", "decode_step",
-           "decode_step_fused"]
+           "decode_step_fused", "decode_step_noalloc"]
 
 
 def _i32p(a: Optional[np.ndarray]):
@@ -259,6 +259,15 @@ def decode_step(pool, layer, p, k_new, v_new, idx_new, q, qidx, widx, table_dev,
     call("tsa_decode_step", pool.handle, int(layer), C.byref(p), _ptr(k_new), _ptr(v_new), _ptr(idx_new),
          _ptr(bad), _ptr(q), _ptr(qidx), _ptr(widx), _ptr(table_dev), int(table_dev.shape[-1]),
          _ptr(seq_lens), _ptr(out), _ptr(topk_out), _ptr(workspace), _nbytes(workspace), _stream(stream))
+
+
+def decode_step_noalloc(pool, layer, p, k_new, v_new, idx_new, q, qidx, widx, table_dev, seq_lens, out,
+                        topk_out=None, bad=None, stream=None):
+    """tsa_decode_step with the library's own scratch array as the workspace (no allocation;
+    calls that overlap on one GPU race; see tsa_decode_step_noalloc)."""
+    call("tsa_decode_step_noalloc", pool.handle, int(layer), C.byref(p), _ptr(k_new), _ptr(v_new),
+         _ptr(idx_new), _ptr(bad), _ptr(q), _ptr(qidx), _ptr(widx), _ptr(table_dev),
+         int(table_dev.shape[-1]), _ptr(seq_lens), _ptr(out), _ptr(topk_out), _stream(stream))
 
 
 def decode_step_fused(pool, layer, p, k_new, v_new, idx_new, q, qidx, widx, table_dev, seq_lens, out,

@@ -61,6 +61,8 @@ SIGNATURES = {
                                      vp, sz, vp]),
     "tsa_decode_step": (i32, [vp, i32, C.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
                               vp, vp, vp, sz, vp]),
+    "tsa_decode_step_noalloc": (i32, [vp, i32, C.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp, vp, vp,
+                                      i32, vp, vp, vp, vp]),
     "tsa_decode_step_fused": (i32, [vp, i32, C.POINTER(DecodeParams), vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                     vp, vp, vp, vp]),
     "tsa_step_graph_create": (i32, [vp, i32, C.POINTER(DecodeParams), C.POINTER(AppendArgs), vp, vp, vp,

@@ -2,10 +2,43 @@
 // stream.  The step is the GLM5.3 sparse-attention page's DSA decode: lightning-indexer score
 // of every cached token, top-k selection, attention over the selected tokens only.
 #include <algorithm>
+#include <mutex>
 
 #include "tsa_internal.h"
 
 using tsa::fail;
+
+// Scratch memory of tsa_decode_step_noalloc: a workspace that the library owns, for callers that
+// cannot allocate.  Each GPU the library runs on holds its own copy of this array from the time the
+// library's code is loaded on it until the process ends.  In host code `scratch` names a host-side
+// stand-in, not the device array: kernels must receive the address hipGetSymbolAddress reports for
+// the current device, which is looked up once per device and kept in scratch_dev.
+namespace {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first call per device).
+tsa_status current_scratch(void** out) {
+    int dev = -1;
+    tsa_status st = tsa::hip_check(hipGetDevice(&dev), "hipGetDevice");
+    if (st) return st;
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(TSA_ERR_UNSUPPORTED, "device index " + std::to_string(dev) + " above 63");
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void* ptr = nullptr;
+        st = tsa::hip_check(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (st) return st;
+        if (!ptr) return fail(TSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        scratch_dev[dev] = ptr;
+    }
+    *out = scratch_dev[dev];
+    return TSA_OK;
+}
+}  // namespace
 
 namespace {
 
@@ -240,6 +273,27 @@ tsa_status tsa_decode_step(tsa_kv_pool* pool, int32_t layer, const tsa_decode_pa
                                   seq_lens_dev, out_dev,
                                   plan.partial_bytes ? at(workspace, w.partial) : nullptr, s);
     return tsa::hip_check(e, "decode step launch");
+}
+
+tsa_status tsa_decode_step_noalloc(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,
+                                   const void* k_new_dev, const void* v_new_dev, const void* idx_new_dev,
+                                   int32_t* bad_dev, const void* q_dev, const void* qidx_dev,
+                                   const float* widx_dev, const int32_t* page_table_dev,
+                                   int32_t max_pages, const int32_t* seq_lens_dev, float* out_dev,
+                                   int32_t* topk_dev, void* stream) {
+    if (!pool || !p) return fail(TSA_ERR_INVALID, "NULL argument");
+    size_t need = 0;
+    tsa_status st = tsa_sparse_decode_workspace(pool, p, &need);
+    if (st) return st;
+    if (need > kScratchBytes)
+        return fail(TSA_ERR_CAPACITY, "the step needs " + std::to_string(need) +
+                                          " bytes of workspace; tsa_decode_step_noalloc holds " +
+                                          std::to_string(kScratchBytes) + " (use tsa_decode_step)");
+    void* ws = nullptr;
+    if ((st = current_scratch(&ws))) return st;
+    return tsa_decode_step(pool, layer, p, k_new_dev, v_new_dev, idx_new_dev, bad_dev, q_dev, qidx_dev,
+                           widx_dev, page_table_dev, max_pages, seq_lens_dev, out_dev, topk_dev, ws,
+                           kScratchBytes, stream);
 }
 
 tsa_status tsa_decode_step_fused(tsa_kv_pool* pool, int32_t layer, const tsa_decode_params* p,

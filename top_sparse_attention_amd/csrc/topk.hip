@@ -1,30 +1,45 @@
-// Top-k selection of indexer scores: one workgroup per request, radix select in LDS.
+// Top-k selection of indexer scores: one workgroup per request.
 //
 // GLM5.3 sparse-attention page, lightning-indexer paragraph: the score selects the top K
 // tokens; a query with fewer than K tokens stays dense.  Equal scores are ordered by position
 // (lowest first), so the selected set is unique; it is written as ascending positions.
 //
-// Method: scores map to order-preserving 32-bit keys.  Four 8-bit radix passes narrow the key
-// of the k-th largest element (a histogram of the candidate digits per pass, kept in LDS as 16
-// interleaved copies so that lanes hitting the same bin spread over distinct addresses).  A pass
-// also finds the smallest and largest candidate key; when they are equal the threshold key is
-// known and the remaining passes are skipped (ties at the threshold are common for
-// integer-valued scores).  The pass is latency-bound, so it keeps workgroup barriers few: the
-// histogram and the key-range slots are double-buffered by pass parity (the next pass's copy
-// is cleared during the current one), and the wave-level scans and min / max use DPP lane
-// moves rather than LDS round trips.  After the passes, every element whose key exceeds the threshold is
-// kept, and of the elements equal to it the lowest positions fill the rest; a prefix count in
-// position order of the packed counts (above, equal) yields both the tie ranks and the output
-// offsets, so the output comes out ascending with no sort.  Each wave owns a contiguous block of
-// positions and reads it with wave-contiguous 16-byte loads (one 1 KiB run per instruction);
-// the prefix is then a wave scan per load group plus one block scan of the wave totals.
+// Scores map to order-preserving 32-bit keys, 32 to 64 per thread in registers.  One workgroup
+// holds a whole request, so what the kernel costs is the vector-ALU work per element: it makes one
+// cheap pass over all elements and does the exact selection on a short list.
+//  1. Sample: one key per thread (1,024 regularly spaced positions).  A histogram of the sample's
+//     12-bit first digits (sign, exponent, top three mantissa bits) gives a bound t_lo: the lower
+//     edge of the bin holding the sample's r-th largest key, with r the sample's expected share
+//     of the k kept elements plus four standard deviations.  The k largest keys of the request are
+//     then almost surely all >= t_lo.
+//  2. One pass in position order compacts every element with key >= t_lo (key and position) into
+//     an LDS list, its place given by a prefix count: a wave scan per load group plus one block
+//     scan of the wave totals.  Each wave owns a contiguous block of positions and reads it with
+//     wave-contiguous 16-byte loads (one 1 KiB run per instruction).
+//  3. If the list holds at least k and at most 8,192 elements, the selection runs on it alone,
+//     8 per thread in list order (which is position order): radix passes narrow the key of the
+//     k-th largest (a 12-bit digit, then 8, 8 and 4 bits; a pass stops the search once the
+//     remaining candidates are equal or their bin is kept whole), then a prefix count in list
+//     order of the packed pair (above the threshold, equal to it) gives the tie ranks and the
+//     output offsets at once, so the output comes out ascending with no sort.
+//  4. Otherwise (an unlucky sample, heavy ties, a crowded range) the same selection runs over
+//     every element in registers with 8-bit digits from the top.
+// Radix-pass histograms are LDS atomics on interleaved copies, so that lanes hitting one bin
+// spread over banks; consecutive passes double-buffer their histograms and key-range slots by
+// parity to save barriers, and wave scans and min / max use DPP lane moves.
 #include "tsa_internal.h"
 
 namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kCopies = 16;
+constexpr int kCopies = 16;               // histogram copies of the 8-bit passes
+constexpr int kBins1 = 4096;              // 12-bit digit: key bits 31..20
+constexpr int kShift1 = 20;
+constexpr int kCopies12 = 2;              // histogram copies of the list's 12-bit pass
+constexpr int kListCap = 8192;            // list entries (keys, then positions, in `big`)
+constexpr int kPer = kListCap / kThreads; // list entries per thread
+static_assert(kBins1 * kCopies12 <= 2 * kListCap, "the 12-bit histogram fits where the list was");
 
 __device__ inline uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -98,11 +113,12 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
                                                               const int32_t* __restrict__ seq_lens,
                                                               int max_len, int k,
                                                               int32_t* __restrict__ out) {
-    __shared__ uint32_t hist[2][256 * kCopies];    // one buffer per pass parity
+    // the sample histogram, then the list (keys | positions), then the list's 12-bit histogram
+    __shared__ uint32_t big[2 * kListCap];
+    __shared__ uint32_t hist[2][256 * kCopies];    // 8-bit passes, one buffer per pass parity
     __shared__ int sh_scan[2][2 * kWaves + 1];
     __shared__ int sh_sel[4];
     __shared__ uint32_t sh_mm[4];                  // candidate key range, per pass parity
-
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     int len = seq_lens[b];
@@ -150,6 +166,233 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
     }
     auto valid = [&](int i) { return wbase + 64 * E * (i / E) + (i % E) < len; };
 
+
+    // ---- 1. sample: element 0 of every thread; t_lo from its 12-bit digit histogram ----
+    for (int i = tid; i < kBins1; i += kThreads) big[i] = 0;
+    for (int i = tid; i < 256 * kCopies; i += kThreads) hist[0][i] = 0;
+    if (tid == 0) {
+        sh_mm[0] = 0xffffffffu;
+        sh_mm[1] = 0u;
+    }
+    __syncthreads();
+    if (valid(0)) atomicAdd(&big[key[0] >> kShift1], 1u);
+    __syncthreads();
+    {
+        uint32_t c[4];
+        int t = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            c[e] = big[kBins1 - 1 - 4 * tid - e];
+            t += int(c[e]);
+        }
+        int n_s;
+        int above = block_exclusive_scan(t, sh_scan[1], &n_s);
+        // the sample's expected count of kept elements, plus four standard deviations and a floor
+        const float expect = float(k) * float(n_s) / float(len);
+        const int r = min(n_s, int(ceilf(expect + 4.f * sqrtf(expect))) + 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (above < r && above + int(c[e]) >= r) sh_sel[0] = kBins1 - 1 - 4 * tid - e;
+            above += int(c[e]);
+        }
+    }
+    __syncthreads();
+    const uint32_t t_lo = uint32_t(sh_sel[0]) << kShift1;
+
+    // ---- 2. compact the elements with key >= t_lo, in position order ----
+    int n_keep;
+    {
+        uint32_t cnt[G], pre[G];
+        uint32_t run = 0;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) c += (valid(E * g + e) && key[E * g + e] >= t_lo) ? 1u : 0u;
+            cnt[g] = c;
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const uint32_t x = wave_inclusive_sum(cnt[g]);
+            pre[g] = run + x - cnt[g];
+            run += uint32_t(__builtin_amdgcn_readlane(int(x), 63));
+        }
+        const uint32_t wave_pre = uint32_t(block_exclusive_scan(lane == 63 ? int(run) : 0, sh_scan[0], &n_keep));
+        // the sample histogram (aliased by the list) was last read before the scan's barriers
+        if (n_keep >= k && n_keep <= kListCap) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                int idx = int(wave_pre + pre[g]);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const int i = E * g + e;
+                    if (valid(i) && key[i] >= t_lo) {
+                        if (idx < kListCap) {
+                            big[idx] = key[i];
+                            big[kListCap + idx] = uint32_t(wbase + 64 * E * g + e);
+                        }
+                        ++idx;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    if (n_keep >= k && n_keep <= kListCap) {     // uniform
+        // ---- 3. select on the list: thread t holds entries kPer t .. kPer t + kPer - 1 ----
+        uint32_t lk[kPer];
+        int32_t lp[kPer];
+        bool lv[kPer];
+        uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int idx = kPer * tid + j;
+            lv[j] = idx < n_keep;
+            lk[j] = lv[j] ? big[idx] : 0u;
+            lp[j] = lv[j] ? int32_t(big[kListCap + idx]) : 0;
+            if (lv[j]) {
+                kmin = min(kmin, lk[j]);
+                kmax = max(kmax, lk[j]);
+            }
+        }
+        kmin = wave_min(kmin);
+        kmax = wave_max(kmax);
+        if (lane == 0) {
+            atomicMin(&sh_mm[0], kmin);
+            atomicMax(&sh_mm[1], kmax);
+        }
+        __syncthreads();                 // the list is in registers; `big` is free again
+        uint32_t prefix = 0, mask = 0;
+        int remaining = k;               // how many of the entries matching `prefix` under `mask` to keep
+        int pass = 0;
+        bool done = false;
+        if (sh_mm[0] == sh_mm[1]) {      // uniform: every entry has the same key
+            prefix = sh_mm[0];
+            mask = 0xffffffffu;
+            done = true;
+        } else {
+            // 12-bit first digit
+            uint32_t* h12 = big;
+            for (int i = tid; i < kBins1 * kCopies12; i += kThreads) h12[i] = 0;
+            if (tid == 0) {
+                sh_mm[2] = 0xffffffffu;
+                sh_mm[3] = 0u;
+            }
+            __syncthreads();
+            const int copy = tid & (kCopies12 - 1);
+#pragma unroll
+            for (int j = 0; j < kPer; ++j)
+                if (lv[j]) atomicAdd(&h12[(lk[j] >> kShift1) * kCopies12 + copy], 1u);
+            __syncthreads();
+            uint32_t c[4];
+            int t = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int dgt = kBins1 - 1 - 4 * tid - e;
+                c[e] = 0;
+#pragma unroll
+                for (int j = 0; j < kCopies12; ++j) c[e] += h12[dgt * kCopies12 + j];
+                t += int(c[e]);
+            }
+            int total;
+            int above = block_exclusive_scan(t, sh_scan[1], &total);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (above < remaining && above + int(c[e]) >= remaining) {
+                    sh_sel[0] = kBins1 - 1 - 4 * tid - e;
+                    sh_sel[1] = remaining - above;
+                    sh_sel[2] = int(c[e]);
+                }
+                above += int(c[e]);
+            }
+            __syncthreads();
+            prefix = uint32_t(sh_sel[0]) << kShift1;
+            mask = 0xfff00000u;
+            remaining = sh_sel[1];
+            done = sh_sel[2] == remaining;       // the whole bin is kept
+            __syncthreads();
+        }
+        // 8, 8 and 4 more bits over the entries still matching
+        for (int shift = 12; !done && shift >= -4; shift -= 8, ++pass) {
+            const int sh = shift > 0 ? shift : 0;
+            const uint32_t width_mask = shift > 0 ? 255u : 15u;
+            uint32_t* h = hist[pass & 1];
+            // the other buffer was last read before the previous pass's selection barrier
+            for (int i = tid; i < 256 * kCopies; i += kThreads) hist[(pass + 1) & 1][i] = 0;
+            const int copy = tid & (kCopies - 1);
+            uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                if (lv[j] && (lk[j] & mask) == prefix) {
+                    atomicAdd(&h[((lk[j] >> sh) & width_mask) * kCopies + copy], 1u);
+                    lo = min(lo, lk[j]);
+                    hi = max(hi, lk[j]);
+                }
+            }
+            lo = wave_min(lo);
+            hi = wave_max(hi);
+            const int slot = 2 * ((pass + 1) & 1);   // sh_mm[0..1] held the whole list's range
+            if (lane == 0) {
+                atomicMin(&sh_mm[slot], lo);
+                atomicMax(&sh_mm[slot + 1], hi);
+            }
+            if (tid == 0) {
+                sh_mm[2 * (pass & 1)] = 0xffffffffu;
+                sh_mm[2 * (pass & 1) + 1] = 0u;
+            }
+            __syncthreads();
+            if (sh_mm[slot] == sh_mm[slot + 1]) {      // uniform
+                prefix = sh_mm[slot];
+                mask = 0xffffffffu;
+                break;
+            }
+            int cb = 0;
+            if (tid < 256) {
+                const int dgt = 255 - tid;
+#pragma unroll
+                for (int j = 0; j < kCopies; ++j) cb += h[dgt * kCopies + ((j + tid) & (kCopies - 1))];
+            }
+            int total;
+            const int above = block_exclusive_scan(cb, sh_scan[pass & 1], &total);
+            if (tid < 256 && above < remaining && above + cb >= remaining) {
+                sh_sel[0] = 255 - tid;
+                sh_sel[1] = remaining - above;
+                sh_sel[2] = cb;
+            }
+            __syncthreads();
+            const uint32_t dgt = uint32_t(sh_sel[0]);
+            remaining = sh_sel[1];
+            const int bin_count = sh_sel[2];
+            __syncthreads();
+            prefix |= dgt << sh;
+            mask |= width_mask << sh;
+            if (bin_count == remaining) break;
+        }
+        // kept entries in list order: above the threshold, or equal to it and among the first
+        // `remaining` equal ones; packed (above << 16 | equal) counts, both below 2^16 here
+        uint32_t cc = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const uint32_t m = lk[j] & mask;
+            cc += (lv[j] && m > prefix) ? 0x10000u : 0u;
+            cc += (lv[j] && m == prefix) ? 1u : 0u;
+        }
+        int total;
+        const uint32_t cpre = uint32_t(block_exclusive_scan(int(cc), sh_scan[pass & 1], &total));
+        int gt = int(cpre >> 16), eq = int(cpre & 0xffffu);
+        int off = gt + min(eq, remaining);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const uint32_t m = lk[j] & mask;
+            bool take = lv[j] && m > prefix;
+            if (lv[j] && m == prefix) take = eq++ < remaining;
+            if (take && off < k) o[off++] = lp[j];
+        }
+        return;
+    }
+
+    // ---- 4. general path: 8-bit radix passes over every element, then the selection ----
     uint32_t prefix = 0, mask = 0;
     int remaining = k;  // how many of the elements matching `prefix` under `mask` to keep
     for (int i = tid; i < 256 * kCopies; i += kThreads) hist[0][i] = 0;

@@ -386,8 +386,30 @@ tsa_status tsa_lru_fetch(tsa_lru* lru, int32_t n_req, const int32_t* slot_table,
                          int32_t* slot_table_dev, void* workspace, size_t ws_bytes,
                          void* stream);
 
-/* Unpin the pages held under `tag`. */
+/* Unpin the pages held under `tag`.  The caller orders any later fetch after every kernel that
+ * reads those pages (tsa_lru_release_layer does it for the caller). */
 tsa_status tsa_lru_release(tsa_lru* lru, int64_t tag);
+
+/* [GLM5.3 page], HiSparse paragraph: layer N's loads overlap layer N-1's compute, so a slot may be
+ * given to a new page while the attention that read its old page is still queued.  This call
+ * unpins the pages held under `tag` now (a later plan may evict them) and makes every later fetch
+ * (tsa_lru_fetch, tsa_lru_prefetch) wait on its stream for `done_event` before it copies anything:
+ * record done_event right after the last kernel that reads the tag's slots (e.g. that layer's
+ * attention), on that kernel's stream.  A copy can then never overwrite a slot before that kernel
+ * is done ([snapshot page], "Ba thứ chặn đường": a write through a stale slot goes to the wrong
+ * place without any error).  done_event (a hipEvent_t, caller-owned, nullable = tsa_lru_release)
+ * must stay valid until the next fetch call returns; recording it again later only makes that
+ * fetch wait longer. */
+tsa_status tsa_lru_release_layer(tsa_lru* lru, int64_t tag, void* done_event);
+
+/* Plan and fetch one layer in one call, ordered for the caller: tsa_lru_plan (no host table),
+ * then tsa_lru_fetch on `stream` (after the events of released tags, as above), then
+ * fetched_event (a hipEvent_t, caller-owned, nullable) recorded on `stream`: the attention of
+ * the layer waits on it (hipStreamWaitEvent) so that it never reads a slot whose copy is still
+ * in flight.  Argument errors are reported before the plan changes anything. */
+tsa_status tsa_lru_prefetch(tsa_lru* lru, int32_t layer, int64_t tag, int32_t n_req,
+                            const int32_t* positions, int32_t k, int32_t* slot_table_dev,
+                            void* workspace, size_t ws_bytes, void* stream, void* fetched_event);
 
 /* Counters since creation (preloads excluded): page touches that hit, that missed, evictions,
  * and bytes copied from host memory (preloads included). */

@@ -52,6 +52,16 @@ def _stream(stream) -> Optional[int]:
     return int(torch.cuda.current_stream().cuda_stream)
 
 
+def _event(ev) -> Optional[int]:
+    """Raw hipEvent_t of a torch.cuda.Event (or None)."""
+    if ev is None:
+        return None
+    h = int(ev.cuda_event)
+    if not h:
+        raise ValueError("the event has not been recorded yet")
+    return h
+
+
 def abi_version() -> int:
     return int(load().tsa_abi_version())
 
@@ -216,6 +226,26 @@ class LruTier:
 
     def release(self, tag: int):
         call("tsa_lru_release", self.handle, int(tag))
+
+    def release_layer(self, tag: int, done=None):
+        """Unpin ``tag``'s pages; later fetches wait for ``done`` (a torch.cuda.Event recorded
+        after the last kernel that reads those pages) before copying (tsa_lru_release_layer)."""
+        call("tsa_lru_release_layer", self.handle, int(tag), _event(done))
+
+    def prefetch(self, layer: int, tag: int, positions: np.ndarray, table_dev, stream=None, fetched=None):
+        """Plan and fetch one layer on ``stream`` (after the events of released tags), then record
+        ``fetched`` (a torch.cuda.Event) there (tsa_lru_prefetch)."""
+        import torch
+        positions = np.ascontiguousarray(positions, dtype=np.int32)
+        n_req, k = positions.shape
+        if self.workspace is None:
+            self.workspace = torch.empty(max(self.workspace_bytes(n_req), 256), dtype=torch.uint8,
+                                         device=self.cache.k.device)
+        if fetched is not None and not fetched.cuda_event:
+            fetched.record(torch.cuda.current_stream() if stream is None else stream)   # creates it
+        call("tsa_lru_prefetch", self.handle, int(layer), int(tag), int(n_req), _i32p(positions), int(k),
+             _ptr(table_dev), _ptr(self.workspace), _nbytes(self.workspace), _stream(stream),
+             _event(fetched))
 
     def stats(self):
         v = [_lib.i64() for _ in range(4)]

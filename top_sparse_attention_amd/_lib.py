@@ -76,6 +76,8 @@ SIGNATURES = {
     "tsa_lru_workspace_bytes": (i32, [vp, i32, P_sz]),
     "tsa_lru_fetch": (i32, [vp, i32, P_i32, vp, vp, sz, vp]),
     "tsa_lru_release": (i32, [vp, i64]),
+    "tsa_lru_release_layer": (i32, [vp, i64, vp]),
+    "tsa_lru_prefetch": (i32, [vp, i32, i64, i32, P_i32, i32, vp, vp, sz, vp, vp]),
     "tsa_lru_stats": (i32, [vp, P_i64, P_i64, P_i64, P_i64]),
 }
 

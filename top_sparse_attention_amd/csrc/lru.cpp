@@ -47,6 +47,9 @@ struct tsa_lru {
     int32_t head = -1, tail = -1;
     int64_t n_evictable = 0;
     std::unordered_map<int64_t, std::vector<int32_t>> held;   // tag -> pinned slots
+    // caller events of released tags: the next fetch's copies may reuse those tags' slots, so
+    // they wait for these first
+    std::vector<hipEvent_t> wait_events;
     uint64_t clock = 0;
     int64_t hits = 0, misses = 0, evictions = 0, h2d_bytes = 0;
 
@@ -374,6 +377,17 @@ tsa_status tsa_lru_release(tsa_lru* l, int64_t tag) {
     TSA_GUARD_END
 }
 
+tsa_status tsa_lru_release_layer(tsa_lru* l, int64_t tag, void* done_event) {
+    TSA_GUARD_BEGIN
+    if (!l) return fail(TSA_ERR_INVALID, "null argument");
+    if (!l->held.count(tag)) return fail(TSA_ERR_INVALID, "tag not held");
+    hipEvent_t ev = static_cast<hipEvent_t>(done_event);
+    if (ev && std::find(l->wait_events.begin(), l->wait_events.end(), ev) == l->wait_events.end())
+        l->wait_events.push_back(ev);
+    return tsa_lru_release(l, tag);
+    TSA_GUARD_END
+}
+
 tsa_status tsa_lru_workspace_bytes(const tsa_lru* l, int32_t n_req, size_t* bytes) {
     if (!l || !bytes || n_req < 0) return fail(TSA_ERR_INVALID, "bad arguments");
     // a fetch carries at most the cache's capacity of copies and of table entries
@@ -382,19 +396,30 @@ tsa_status tsa_lru_workspace_bytes(const tsa_lru* l, int32_t n_req, size_t* byte
     return TSA_OK;
 }
 
+namespace {
+
+// Argument checks of a fetch that do not depend on the plan (no side effects).
+tsa_status fetch_args_ok(const tsa_lru* l, int32_t n_req, const int32_t* slot_table_dev,
+                         const void* workspace, size_t ws_bytes) {
+    if (!l || (n_req > 0 && !slot_table_dev) || n_req < 0 || n_req > l->num_req)
+        return fail(TSA_ERR_INVALID, "bad arguments");
+    if (!l->host_k) return fail(TSA_ERR_INVALID, "a bookkeeping-only tier cannot fetch");
+    if (workspace && ws_bytes < ws_bytes_total(l->capacity)) return fail(TSA_ERR_CAPACITY, "workspace too small");
+    return TSA_OK;
+}
+
+}  // namespace
+
 tsa_status tsa_lru_fetch(tsa_lru* l, int32_t n_req, const int32_t* slot_table,
                          int32_t* slot_table_dev, void* workspace, size_t ws_bytes, void* stream) {
     TSA_GUARD_BEGIN
-    if (!l || (n_req > 0 && !slot_table_dev) || n_req < 0 || n_req > l->num_req)
-        return fail(TSA_ERR_INVALID, "bad arguments");
     (void)slot_table;   // the entries come from the plan itself
-    if (!l->host_k) return fail(TSA_ERR_INVALID, "a bookkeeping-only tier cannot fetch");
+    tsa_status chk = fetch_args_ok(l, n_req, slot_table_dev, workspace, ws_bytes);
+    if (chk) return chk;
     const int64_t n = int64_t(l->pending_slots.size());
     const int64_t n_tab = int64_t(l->plan_index.size());
     if ((n > 0 || n_tab > 0) && !workspace) return fail(TSA_ERR_INVALID, "workspace required");
     if (n > l->capacity || n_tab > l->capacity) return fail(TSA_ERR_INVALID, "more pending copies than slots");
-    if ((n > 0 || n_tab > 0) && ws_bytes < ws_bytes_total(l->capacity))
-        return fail(TSA_ERR_CAPACITY, "workspace too small");
     for (int64_t i = 0; i < n_tab; ++i)
         if (l->plan_index[size_t(i)] >= int64_t(n_req) * l->pages_per_req)
             return fail(TSA_ERR_INVALID, "the last plan covered more requests than n_req");
@@ -440,6 +465,11 @@ tsa_status tsa_lru_fetch(tsa_lru* l, int32_t n_req, const int32_t* slot_table,
         std::memcpy(htab, l->plan_slot.data(), size_t(n_tab) * 4);
     }
     tsa_status e = TSA_OK;
+    // copies may land in slots of tags released with an event: wait for those first
+    for (hipEvent_t ev : l->wait_events)
+        if (e == TSA_OK) e = tsa::hip_check(hipStreamWaitEvent(s, ev, 0), "hipStreamWaitEvent");
+    if (e != TSA_OK) return e;
+    l->wait_events.clear();
     if (n + n_tab > 0) {
         unsigned char* w = static_cast<unsigned char*>(workspace);
         int64_t* dkeys = reinterpret_cast<int64_t*>(w);
@@ -460,6 +490,22 @@ tsa_status tsa_lru_fetch(tsa_lru* l, int32_t n_req, const int32_t* slot_table,
     l->pending_slots.clear();
     l->plan_index.clear();
     l->plan_slot.clear();
+    return TSA_OK;
+    TSA_GUARD_END
+}
+
+tsa_status tsa_lru_prefetch(tsa_lru* l, int32_t layer, int64_t tag, int32_t n_req,
+                            const int32_t* positions, int32_t k, int32_t* slot_table_dev,
+                            void* workspace, size_t ws_bytes, void* stream, void* fetched_event) {
+    TSA_GUARD_BEGIN
+    tsa_status st = fetch_args_ok(l, n_req, slot_table_dev, workspace, ws_bytes);
+    if (st) return st;
+    if (!workspace) return fail(TSA_ERR_INVALID, "workspace required");
+    if ((st = tsa_lru_plan(l, layer, tag, n_req, positions, k, nullptr, nullptr))) return st;
+    if ((st = tsa_lru_fetch(l, n_req, nullptr, slot_table_dev, workspace, ws_bytes, stream))) return st;
+    if (fetched_event)
+        return tsa::hip_check(hipEventRecord(static_cast<hipEvent_t>(fetched_event), static_cast<hipStream_t>(stream)),
+                              "hipEventRecord");
     return TSA_OK;
     TSA_GUARD_END
 }

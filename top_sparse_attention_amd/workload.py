@@ -7,6 +7,7 @@ decode step needs.  Nothing here computes any part of the step itself.
 from __future__ import annotations
 
 import dataclasses
+import os
 from typing import Optional
 
 import numpy as np
@@ -202,12 +203,18 @@ def stage_tier(w, seed: int = 0, num_req: Optional[int] = None, length: Optional
     host_v = torch.empty((keys * P, row), dtype=torch.bfloat16, pin_memory=True)
     hk = host_k.view(torch.int16).numpy()
     hv = host_v.view(torch.int16).numpy()
-    for layer in range(NL):
-        for r in range(R):
-            _, kk, vv = synth.request_tokens(w, seed, r, L, layer=layer)
-            base = ((layer * R + r) * npr) * P
-            hk[base:base + L] = kk.reshape(L, row).view(np.int16)
-            hv[base:base + L] = vv.reshape(L, row).view(np.int16)
+
+    def fill(lr):
+        layer, r = lr
+        _, kk, vv = synth.request_tokens(w, seed, r, L, layer=layer)
+        base = ((layer * R + r) * npr) * P
+        hk[base:base + L] = kk.reshape(L, row).view(np.int16)
+        hv[base:base + L] = vv.reshape(L, row).view(np.int16)
+
+    # every (layer, request) has its own generators, so the draws can run side by side
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(min(16, max(1, len(os.sched_getaffinity(0))))) as ex:
+        list(ex.map(fill, [(layer, r) for layer in range(NL) for r in range(R)]))
     if unit == "token":
         C, P, npr = C * P, 1, npr * P
     elif unit != "page":

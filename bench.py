@@ -99,6 +99,33 @@ def _oracle_rate(w, seed: int, budget_s: float):
                           f"oracle time; input generation not timed")
 
 
+def _mem_available() -> int:
+    """MemAvailable of this host in bytes (0 when unknown)."""
+    try:
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemAvailable:"):
+                return int(line.split()[1]) * 1024
+    except Exception:
+        pass
+    return 0
+
+
+def _probe_pinned(want: int, chunk: int = 4 << 30) -> int:
+    """Bytes of pinned host memory this process can hold, up to `want`: pins 4 GiB blocks until
+    the runtime refuses or `want` is reached, then frees them (and torch's pinned-block cache)."""
+    import torch
+    held, total = [], 0
+    try:
+        while total < want:
+            held.append(torch.empty(chunk, dtype=torch.uint8, pin_memory=True))
+            total += chunk
+    except Exception:
+        pass
+    del held
+    torch._C._host_emptyCache()
+    return total
+
+
 def cpu_baseline(w, seed: int, budget_s: float = 12.0):
     """The oracle as it stands, timed on this host on a bounded sample of the same workload
     (whole requests: scores over every token, full-sort top-k, float64 attention), twice: with
@@ -369,14 +396,29 @@ def bench_tier(args):
 
     tsa.load()
     w = synth.get(args.workload)
-    R = args.tier_requests
     L = int(w.fixed_lens[0])
     NL, P, k = w.num_layers, w.page_size, w.top_k
+    row = w.num_kv_heads * w.head_dim_k
+    per_req = 2 * NL * L * row * 2                 # pinned host bytes of one request (K and V)
+    R = args.tier_requests or w.batch
+    avail = _mem_available()
+    fit = int(avail // 2 // per_req) if avail else R
+    reduced = fit < R
+    if reduced:
+        print(f"[bench] tier: {R} requests need {R * per_req / 2**30:.1f} GiB pinned; half of the "
+              f"{avail / 2**30:.1f} GiB available holds {fit}", file=sys.stderr, flush=True)
+        R = max(1, fit)
+    # pinned host memory has its own limit below the host's memory: find what can be pinned
+    pinnable = _probe_pinned(R * per_req + (4 << 30))
+    if pinnable < R * per_req + (4 << 30):
+        fit = max(1, int((pinnable - (4 << 30)) // per_req))
+        print(f"[bench] tier: {pinnable / 2**30:.0f} GiB could be pinned; {R} requests need "
+              f"{R * per_req / 2**30:.1f} GiB (+4 GiB headroom): running {fit}", file=sys.stderr, flush=True)
+        R, reduced = fit, True
     w = dataclasses.replace(w, batch=R, fixed_lens=(L,) * R)
     npr = -(-L // P)
     keys = NL * R * npr
     C = int(round(keys * w.cache_fraction))
-    row = w.num_kv_heads * w.head_dim_k
     print(f"[bench] tier: {R} requests x {L} tokens x {NL} layers, {keys} pages "
           f"({2 * keys * P * row * 2 / 2**30:.1f} GiB pinned), cache {C} slots", file=sys.stderr, flush=True)
     g = torch.Generator().manual_seed(args.seed)
@@ -387,11 +429,13 @@ def bench_tier(args):
     block = torch.empty(1 << 25, dtype=torch.bfloat16)
     for i in range(0, block.numel(), 1 << 22):
         block[i:i + (1 << 22)].normal_(0.0, w.kv_std, generator=g)
-    for t in (host_k, host_v):
+    for name, t in (("K", host_k), ("V", host_v)):
         flat = t.view(-1)
         for i in range(0, flat.numel(), block.numel()):
             n = min(block.numel(), flat.numel() - i)
             flat[i:i + n].copy_(block[:n])
+            if (i // block.numel()) % 256 == 255:
+                print(f"[bench] tier: host {name} filled {(i + n) * 2 / 2**30:.0f} GiB", file=sys.stderr, flush=True)
     # the cache unit: whole pages, or single token rows (a pool of one-token pages holding the
     # same bytes); the host copy is the same either way
     CP, UP, unpr = (C, P, npr) if args.tier_unit == "page" else (C * P, 1, npr * P)
@@ -455,7 +499,7 @@ def bench_tier(args):
     fetched = [torch.cuda.Event() for _ in range(2)]
     done = {}
     ev_attn = []
-    host_s = {"plan": 0.0, "fetch": 0.0}
+    host_s = {"prefetch": 0.0}
     gidx = 0
 
     def run_step(step, timed):
@@ -470,16 +514,12 @@ def bench_tier(args):
                 positions, pos_layer = sh.numpy(), sd
             else:
                 positions, pos_layer = pos_all[step][layer], pos_dev[step][layer]
+            # plan, then the copies on the side stream after the attention of every layer whose
+            # slots they may reuse (released below with its event), then `fetched` recorded there
             h0 = time.perf_counter()
-            tier.plan(layer, gidx, positions, table=False)
-            h1 = time.perf_counter()
-            if gidx - 2 in done:
-                side.wait_event(done[gidx - 2])
-            tier.fetch(table_dev[gidx & 1], stream=side)
+            tier.prefetch(layer, gidx, positions, table_dev[gidx & 1], stream=side, fetched=fetched[gidx & 1])
             if timed:
-                host_s["plan"] += h1 - h0
-                host_s["fetch"] += time.perf_counter() - h1
-            fetched[gidx & 1].record(side)
+                host_s["prefetch"] += time.perf_counter() - h0
             main.wait_event(fetched[gidx & 1])
             e0 = torch.cuda.Event(enable_timing=True) if timed else None
             if timed:
@@ -492,7 +532,7 @@ def bench_tier(args):
             if timed:
                 ev_attn.append((e0, ev))
             if gidx > 0:
-                tier.release(gidx - 1)
+                tier.release_layer(gidx - 1, done[gidx - 1])
             gidx += 1
 
     for s_ in range(args.warmup):
@@ -514,7 +554,9 @@ def bench_tier(args):
         "value": round(R / (ms_step * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "requests": R, "context": L, "layers": NL, "top_k": k,
+        "config": {"workload": w.name, "requests": R, "requests_of_config": synth.get(args.workload).batch,
+                   "requests_reduced_to_fit_pinned_memory": reduced,
+                   "context": L, "layers": NL, "top_k": k,
                    "page_size": P, "cache_unit": args.tier_unit, "cache_slots": CP,
                    "cache_bytes": CP * UP * row * 4, "logical_pages": keys, "q_heads": w.num_q_heads,
                    "kv_heads": w.num_kv_heads, "head_dim": w.head_dim_k, "parallelism": "none",
@@ -522,8 +564,7 @@ def bench_tier(args):
         "tier": {"hit_rate": round(hits / max(hits + misses, 1), 4), "hits": hits, "misses": misses,
                  "h2d_GBps": round(h2d / elapsed / 1e9, 2), "h2d_bytes_per_step": h2d // args.steps,
                  "attention_ms_per_layer": round(attn_ms, 4),
-                 "host_plan_ms_per_step": round(host_s["plan"] * 1e3 / args.steps, 3),
-                 "host_fetch_call_ms_per_step": round(host_s["fetch"] * 1e3 / args.steps, 3)},
+                 "host_prefetch_call_ms_per_step": round(host_s["prefetch"] * 1e3 / args.steps, 3)},
     }
     print(json.dumps(res), flush=True)
 
@@ -540,8 +581,9 @@ def main():
                     help="seconds of oracle time for each of the two host runs (1 thread, all cores)")
     ap.add_argument("--query-sets", type=int, default=8,
                     help="pre-drawn query sets the steps rotate through (different rows per step)")
-    ap.add_argument("--tier-requests", type=int, default=16,
-                    help="requests of the tiered workload (the full 256 needs 128 GiB of pinned memory)")
+    ap.add_argument("--tier-requests", type=int, default=0,
+                    help="requests of the tiered workload (default: the configuration's 256, 128 GiB of "
+                         "pinned host memory; fewer if half of the available host memory cannot hold them)")
     ap.add_argument("--tier-positions", choices=("drawn", "indexer"), default="drawn",
                     help="tiered workload: positions from the seeded locality generator, or from an "
                          "indexer top-k per layer over HBM-resident indexer keys (copied to the host)")

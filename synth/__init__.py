@@ -40,6 +40,9 @@ Workloads (the shapes the pages discuss, with synthetic values):
                      heads each with its own 192-dim key (128 projected + 64
                      rotary) and 128-dim value, top-k 2048.  Keys and values
                      are drawn directly (no trained up-projections).
+* ``mla_b64_32k_h128`` the 64 x 32k latent workload with 128 query heads over the
+                     latent head (GLM5.3 page, roofline paragraph: DeepSeek V3.2 runs
+                     about 128 heads where GLM-5 runs 64).
 * ``tiered_b256_64k`` 256 requests x 65536 tokens x 8 layers; the HBM page
                      cache holds a quarter of the pages (GLM5.3 sparse-attention
                      page, HiSparse paragraph).  Positions come from a seeded
@@ -118,6 +121,8 @@ WORKLOADS = {
                  fixed_lens=(32768,) * 64, reserve=32768),
         Workload("mla_mha_b64_4k", 7, 64, 64, 4160, 64, 64, 192, 128, False, 128, 1, 4, 2048, 0.5, 1.0,
                  fixed_lens=(4096,) * 64, reserve=4096),
+        Workload("mla_b64_32k_h128", 8, 64, 64, 32832, 128, 1, 576, 512, True, 128, 1, 4, 2048, 0.5, 1.0,
+                 fixed_lens=(32768,) * 64, reserve=32768),
         Workload("tiered_b256_64k", 5, 256, 64, 524288, 16, 2, 128, 128, False, 0, 0, 0, 2048, 1.0, 1.0,
                  fixed_lens=(65536,) * 256, num_layers=8, reserve=65536, cache_fraction=0.25),
     ]

@@ -370,6 +370,32 @@ def test_mla_ih64_full_size_all_requests(tsa):
     assert (np.diff(tk, axis=1) > 0).all() and tk.min() >= 0 and tk.max() < 32768
 
 
+@pytest.mark.parametrize("heads", [16, 32, 48, 128])
+def test_mla_head_counts_match_oracle(tsa, heads):
+    """The latent kernel at other query-head counts (GLM5.3 page, roofline paragraph: 64 heads
+    for GLM-5, about 128 for DeepSeek V3.2): 128 heads run as two 64-head blocks, 16 / 32 / 48
+    heads fill one block in part.  4 requests x 32,768 tokens, top-2048, every request checked."""
+    st = staged("mla_b64_32k", {"num_q_heads": heads}, batch=4)
+    assert st.params.num_q_heads == heads
+    sc = _scores_gpu(tsa, st)
+    st.step()
+    torch.cuda.synchronize()
+    errs = _check_all_requests(st, sc)
+    print(f"latent, {heads} heads: max normwise attention error {max(errs):.3e}")
+
+
+def test_mla_h128_full_size_all_requests(tsa):
+    """The 64 x 32k latent workload with 128 query heads, in the benchmark's launch configuration:
+    every request checked whole against the oracle."""
+    st = staged("mla_b64_32k_h128")
+    assert st.params.num_q_heads == 128
+    sc = _scores_gpu(tsa, st)
+    st.step()
+    torch.cuda.synchronize()
+    errs = _check_all_requests(st, sc)
+    print(f"mla_b64_32k_h128: {len(errs)} requests, max normwise attention error {max(errs):.3e}")
+
+
 def test_mla_mha_mode_matches_oracle(tsa):
     """The MHA mode of latent attention (64 heads, each with a 192-dim key and a 128-dim value of
     its own) through the whole step, on the grouped-query kernel with one query head per KV head:

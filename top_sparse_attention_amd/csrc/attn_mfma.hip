@@ -103,13 +103,30 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
     int32_t* pv_seen = flag + 4;                                    // [group] P reads done
     int32_t* rows = pv_seen + kGroups;                              // [chunk]
 
-    const int s_idx = blockIdx.x, b = blockIdx.z;
+    // Unit of this workgroup: (request b, split s_idx, head block hblk of 64 query heads).
+    // Workgroups reach the 8 XCDs round-robin by linear id, so the ids are renumbered to give
+    // each XCD consecutive units, head blocks fastest: the head blocks of one split then read the
+    // same rows through one L2, and a request's splits share its queries there.
+    int s_idx, hblk, b;
+    {
+        const int S = gridDim.x, Y = gridDim.y;
+        const int units = S * Y * int(gridDim.z);
+        const int lin = int(blockIdx.x) + S * (int(blockIdx.y) + Y * int(blockIdx.z));
+        const int u = (units % 8 == 0) ? (lin % 8) * (units / 8) + lin / 8 : lin;
+        hblk = u % Y;
+        s_idx = (u / Y) % S;
+        b = u / (Y * S);
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool is_qk = wave < kGroups;          // uniform
     const int grp = wave & (kGroups - 1);
     const int g16 = lane >> 4, j16 = lane & 15;
-    const int h0 = blockIdx.y * (kGroups * 16) + grp * 16;   // the group's first head
+    const int h0 = hblk * (kGroups * 16) + grp * 16;   // the group's first head
+    // Head counts that are not a multiple of 64 leave the last block's upper groups without
+    // heads: they compute on zero queries (their loads still fill the shared tiles) and store
+    // nothing.
+    const bool active = h0 < a.hq;              // uniform
 
     int len = a.seq_lens[b];
     len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
@@ -347,9 +364,14 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
     // accumulators (PV) never need registers in the same wave.
     const int h = h0 + j16;
     if (is_qk) {
-        const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.hq + h) * DK);
+        if (active) {
+            const uint4* qsrc = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * a.hq + h) * DK);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qreg[ks] = qsrc[ks * 4 + g16];
+            for (int ks = 0; ks < KS; ++ks) qreg[ks] = qsrc[ks * 4 + g16];
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qreg[ks] = make_uint4(0, 0, 0, 0);
+        }
         wait_vm<0>();
         for (int pass = 0; pass < 2; ++pass) {
             scan = false;
@@ -400,7 +422,7 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
         if (g16 == 0) {
             lbuf[(grp * 16 + j16) * 2] = m_ref;
             lbuf[(grp * 16 + j16) * 2 + 1] = l_tot;
-            if (a.splits > 1) {
+            if (a.splits > 1 && active) {
                 const int64_t pidx = (int64_t(b) * a.hq + h) * a.splits + s_idx;
                 // natural-log units, as the combine expects
                 a.part_ml[pidx * 2] = m_ref == -INFINITY ? -INFINITY : m_ref * 0.6931471805599453f;
@@ -441,7 +463,8 @@ __global__ void __launch_bounds__(kThreads, 1) attn_mfma_kernel(MfmaArgs a) {
         }
         __syncthreads();                     // lbuf written
         // lane holds O^T[d = db*16 + 4*g16 + r][head h]
-        if (a.splits == 1) {
+        if (!active) {
+        } else if (a.splits == 1) {
             const float l_tot = lbuf[(grp * 16 + j16) * 2 + 1];
             const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
             float* o = a.out + (int64_t(b) * a.hq + h) * DV;
@@ -470,12 +493,13 @@ size_t mfma_smem(int chunk) {
 
 namespace tsa {
 
-// Shapes the latent kernel handles: values alias the keys, 64 query heads over one latent KV
-// head of 576 dims whose first 512 are the values.
+// Shapes the latent kernel handles: values alias the keys, one latent KV head of 576 dims whose
+// first 512 are the values, and a multiple of 16 query heads (blocks of 64; GLM-5's 64 heads
+// make one block, DeepSeek V3.2's 128 two; 16, 32 or 48 heads fill one block in part).
 bool mfma_latent_applicable(const tsa_kv_pool& pool, const tsa_decode_params& p) {
     const tsa_pool_desc& d = pool.d;
     if (!d.v_from_k || d.head_dim_k != 576 || d.head_dim_v != 512 || d.num_kv_heads != 1) return false;
-    if (p.num_q_heads != 64) return false;
+    if (p.num_q_heads < 16 || p.num_q_heads % 16 || p.num_q_heads > 1024) return false;
     if (pool.slots() >= (int64_t(1) << 31)) return false;   // slots kept as 32-bit in LDS
     int splits = 0;
     const int chunk = mfma_latent_chunk(p, &splits);
@@ -488,7 +512,8 @@ int mfma_latent_chunk(const tsa_decode_params& p, int* splits) {
     // no request selects more than min(top_k, max_len) tokens: split that, not top_k
     const int k_eff = std::max(1, std::min(p.top_k, p.max_len));
     const int tiles = int(ceil_div(k_eff, kTile));
-    int s = int(ceil_div(256, std::max(p.batch, 1)));   // one workgroup per CU
+    const int hblocks = int(ceil_div(p.num_q_heads, kGroups * 16));
+    int s = int(ceil_div(256, std::max(p.batch, 1) * hblocks));   // one workgroup per CU
     s = std::max(1, std::min({s, tiles, 64}));   // the combine takes at most 64 splits
     s = std::max(s, int(ceil_div(tiles, kMaxChunk / kTile)));   // the row list fits in LDS
     const int chunk = int(ceil_div(tiles, s)) * kTile;
@@ -524,7 +549,7 @@ hipError_t launch_attention_mfma(const tsa_kv_pool& pool, int layer, const tsa_d
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
     if (e != hipSuccess) return e;
-    dim3 grid(plan.splits, p.num_q_heads / (kGroups * 16), p.batch);
+    dim3 grid(plan.splits, int(ceil_div(p.num_q_heads, kGroups * 16)), p.batch);
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), smem, s, a);
     return hipGetLastError();
 }

@@ -372,6 +372,7 @@ bool attention_supported(const tsa_kv_pool& pool, const tsa_decode_params& p, st
         *why = "num_q_heads must be a multiple of num_kv_heads";
         return false;
     }
+    if (mfma_latent_applicable(pool, p) || gqa_mfma_applicable(pool, p)) return true;
     const int G = p.num_q_heads / d.num_kv_heads;
     if (ceil_div(int64_t(G) * d.head_dim_v, kThreads) > 128) {
         *why = "query heads per KV head x head_dim_v exceeds 32768";

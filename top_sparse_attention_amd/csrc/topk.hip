@@ -5,8 +5,8 @@
 // (lowest first), so the selected set is unique; it is written as ascending positions.
 //
 // Scores map to order-preserving 32-bit keys, 32 to 64 per thread in registers.  One workgroup
-// holds a whole request, so what the kernel costs is the vector-ALU work per element: it makes one
-// cheap pass over all elements and does the exact selection on a short list.
+// holds a whole request, so what the kernel costs is the instruction count of each wave between
+// barriers: it makes one cheap pass over all elements and does the exact selection on a short list.
 //  1. Sample: one key per thread (1,024 regularly spaced positions).  A histogram of the sample's
 //     12-bit first digits (sign, exponent, top three mantissa bits) gives a bound t_lo: the lower
 //     edge of the bin holding the sample's r-th largest key, with r the sample's expected share
@@ -15,17 +15,20 @@
 //  2. One pass in position order compacts every element with key >= t_lo (key and position) into
 //     an LDS list, its place given by a prefix count: a wave scan per load group plus one block
 //     scan of the wave totals.  Each wave owns a contiguous block of positions and reads it with
-//     wave-contiguous 16-byte loads (one 1 KiB run per instruction).
+//     wave-contiguous 16-byte loads (one 1 KiB run per instruction).  The same pass takes the
+//     request's largest key.
 //  3. If the list holds at least k and at most 8,192 elements, the selection runs on it alone,
-//     8 per thread in list order (which is position order): radix passes narrow the key of the
-//     k-th largest (a 12-bit digit, then 8, 8 and 4 bits; a pass stops the search once the
-//     remaining candidates are equal or their bin is kept whole), then a prefix count in list
-//     order of the packed pair (above the threshold, equal to it) gives the tie ranks and the
-//     output offsets at once, so the output comes out ascending with no sort.
+//     up to 8 per thread in list order (which is position order).  The k-th largest key lies in
+//     [t_lo, largest key]; each pass splits that interval into 4,096 equal bins of keys and keeps
+//     the bin holding the k-th largest, until the bin is one key or is kept whole (at most three
+//     passes).  A bin of dozens of entries is first checked for being one repeated key, which
+//     ends the search on integer-valued scores.  A prefix count in list order of the packed pair
+//     (above the bin, inside it) then gives the tie ranks and the output offsets at once, so the
+//     output comes out ascending with no sort.
 //  4. Otherwise (an unlucky sample, heavy ties, a crowded range) the same selection runs over
 //     every element in registers with 8-bit digits from the top.
-// Radix-pass histograms are LDS atomics on interleaved copies, so that lanes hitting one bin
-// spread over banks; consecutive passes double-buffer their histograms and key-range slots by
+// Histograms are LDS atomics (the 8-bit passes on interleaved copies, so that lanes hitting one
+// bin spread over banks); consecutive passes double-buffer their histograms and scan areas by
 // parity to save barriers, and wave scans and min / max use DPP lane moves.
 #include "tsa_internal.h"
 
@@ -36,10 +39,11 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kCopies = 16;               // histogram copies of the 8-bit passes
 constexpr int kBins1 = 4096;              // 12-bit digit: key bits 31..20
 constexpr int kShift1 = 20;
-constexpr int kCopies12 = 2;              // histogram copies of the list's 12-bit pass
 constexpr int kListCap = 8192;            // list entries (keys, then positions, in `big`)
 constexpr int kPer = kListCap / kThreads; // list entries per thread
-static_assert(kBins1 * kCopies12 <= 2 * kListCap, "the 12-bit histogram fits where the list was");
+constexpr int kTied = 32;                 // a list bin this full is checked for a single key first
+static_assert(kBins1 == 256 * kCopies, "a 12-bit histogram fills one 8-bit pass buffer");
+static_assert(kBins1 <= 2 * kListCap, "the sample histogram fits where the list goes");
 
 __device__ inline uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -113,12 +117,17 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
                                                               const int32_t* __restrict__ seq_lens,
                                                               int max_len, int k,
                                                               int32_t* __restrict__ out) {
-    // the sample histogram, then the list (keys | positions), then the list's 12-bit histogram
-    __shared__ uint32_t big[2 * kListCap];
-    __shared__ uint32_t hist[2][256 * kCopies];    // 8-bit passes, one buffer per pass parity
+    // the sample histogram, then the list: (key, position) pairs
+    __shared__ __align__(16) uint32_t big[2 * kListCap];
+    uint2* list = reinterpret_cast<uint2*>(big);
+    // per pass parity: the general path's 8-bit histograms (kCopies copies of 256 bins) or one
+    // 12-bit histogram of the list (kBins1 bins)
+    __shared__ uint32_t hist[2][256 * kCopies];
     __shared__ int sh_scan[2][2 * kWaves + 1];
-    __shared__ int sh_sel[4];
-    __shared__ uint32_t sh_mm[4];                  // candidate key range, per pass parity
+    __shared__ int sh_sel[2][4];
+    // candidate key ranges: the general path's, per pass parity; the list passes', per pass
+    __shared__ uint32_t sh_mm[4];
+    __shared__ uint32_t sh_kmax;                   // largest key of the request
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     int len = seq_lens[b];
@@ -132,28 +141,27 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
     // Wave w owns the contiguous positions [w * 64 * IPT, (w + 1) * 64 * IPT).  Inside it, element
     // (g, e) of lane l (g < G groups of E values) sits at 64 E g + E l + e: every load instruction
     // of the wave then covers one contiguous run of 64 E values (1 KiB when E = 4), and position
-    // order within the wave is (g, lane, e).
+    // order within the wave is (g, lane, e).  Positions at or past len get key 0.
     constexpr int E = IPT < 4 ? IPT : 4;
     constexpr int G = IPT / E;
     const int lane = tid & 63;
-    const int wbase = (tid >> 6) * 64 * IPT + E * lane;   // position of element (0, 0)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wbase = wave * 64 * IPT + E * lane;   // position of element (0, 0)
     uint32_t key[IPT];
     if (E == 4 && (ld & 3) == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const int p0 = wbase + 64 * E * g;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             if (p0 + 3 < len) {
-                v = *reinterpret_cast<const float4*>(s + p0);
+                const float4 v = *reinterpret_cast<const float4*>(s + p0);
+                key[4 * g + 0] = order_key(v.x);
+                key[4 * g + 1] = order_key(v.y);
+                key[4 * g + 2] = order_key(v.z);
+                key[4 * g + 3] = order_key(v.w);
             } else {
-                if (p0 < len) v.x = s[p0];
-                if (p0 + 1 < len) v.y = s[p0 + 1];
-                if (p0 + 2 < len) v.z = s[p0 + 2];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) key[4 * g + e] = p0 + e < len ? order_key(s[p0 + e]) : 0u;
             }
-            key[4 * g + 0] = order_key(v.x);
-            key[4 * g + 1] = order_key(v.y);
-            key[4 * g + 2] = order_key(v.z);
-            key[4 * g + 3] = order_key(v.w);
         }
     } else {
 #pragma unroll
@@ -166,13 +174,18 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
     }
     auto valid = [&](int i) { return wbase + 64 * E * (i / E) + (i % E) < len; };
 
-
     // ---- 1. sample: element 0 of every thread; t_lo from its 12-bit digit histogram ----
     for (int i = tid; i < kBins1; i += kThreads) big[i] = 0;
-    for (int i = tid; i < 256 * kCopies; i += kThreads) hist[0][i] = 0;
+    for (int i = tid; i < 256 * kCopies; i += kThreads) {
+        hist[0][i] = 0;
+        hist[1][i] = 0;
+    }
     if (tid == 0) {
-        sh_mm[0] = 0xffffffffu;
-        sh_mm[1] = 0u;
+        sh_kmax = 0u;
+        for (int i = 0; i < 4; i += 2) {
+            sh_mm[i] = 0xffffffffu;
+            sh_mm[i + 1] = 0u;
+        }
     }
     __syncthreads();
     if (valid(0)) atomicAdd(&big[key[0] >> kShift1], 1u);
@@ -192,191 +205,154 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
         const int r = min(n_s, int(ceilf(expect + 4.f * sqrtf(expect))) + 16);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            if (above < r && above + int(c[e]) >= r) sh_sel[0] = kBins1 - 1 - 4 * tid - e;
+            if (above < r && above + int(c[e]) >= r) sh_sel[1][0] = kBins1 - 1 - 4 * tid - e;
             above += int(c[e]);
         }
     }
     __syncthreads();
-    const uint32_t t_lo = uint32_t(sh_sel[0]) << kShift1;
+    // at least 1, so that the key 0 of positions past len is never kept (a valid element whose
+    // key is 0 is then missing from the list only when fewer than k keys are >= 1, and the
+    // count check below sends that case to the general path)
+    const uint32_t t_lo = max(uint32_t(sh_sel[1][0]) << kShift1, 1u);
 
     // ---- 2. compact the elements with key >= t_lo, in position order ----
-    int n_keep;
+    // An element's place: earlier waves (one block scan of the wave totals), then earlier groups
+    // of its wave (their totals), then earlier lanes of its group (a wave scan per group).
+    uint32_t n_keep;
     {
         uint32_t cnt[G], pre[G];
-        uint32_t run = 0;
+        uint32_t run = 0, kmx = 0;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             uint32_t c = 0;
 #pragma unroll
-            for (int e = 0; e < E; ++e) c += (valid(E * g + e) && key[E * g + e] >= t_lo) ? 1u : 0u;
+            for (int e = 0; e < E; ++e) {
+                c += key[E * g + e] >= t_lo ? 1u : 0u;
+                kmx = max(kmx, key[E * g + e]);
+            }
             cnt[g] = c;
         }
+        kmx = wave_max(kmx);
+        if (lane == 0) atomicMax(&sh_kmax, kmx);    // read after the scan's barriers
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const uint32_t x = wave_inclusive_sum(cnt[g]);
             pre[g] = run + x - cnt[g];
             run += uint32_t(__builtin_amdgcn_readlane(int(x), 63));
         }
-        const uint32_t wave_pre = uint32_t(block_exclusive_scan(lane == 63 ? int(run) : 0, sh_scan[0], &n_keep));
+        int total;
+        const uint32_t wave_pre = uint32_t(block_exclusive_scan(lane == 63 ? int(run) : 0, sh_scan[0], &total));
+        n_keep = uint32_t(total);
         // the sample histogram (aliased by the list) was last read before the scan's barriers
-        if (n_keep >= k && n_keep <= kListCap) {
+        if (n_keep >= uint32_t(k) && n_keep <= uint32_t(kListCap)) {
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                int idx = int(wave_pre + pre[g]);
+                uint32_t idx = wave_pre + pre[g];
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const int i = E * g + e;
-                    if (valid(i) && key[i] >= t_lo) {
-                        if (idx < kListCap) {
-                            big[idx] = key[i];
-                            big[kListCap + idx] = uint32_t(wbase + 64 * E * g + e);
-                        }
+                    if (key[E * g + e] >= t_lo) {
+                        list[idx] = make_uint2(key[E * g + e], uint32_t(wbase + 64 * E * g + e));
                         ++idx;
                     }
                 }
             }
         }
     }
+    const bool use_list = n_keep >= uint32_t(k) && n_keep <= uint32_t(kListCap);   // uniform
     __syncthreads();
 
-    if (n_keep >= k && n_keep <= kListCap) {     // uniform
-        // ---- 3. select on the list: thread t holds entries kPer t .. kPer t + kPer - 1 ----
+    if (use_list) {
+        // ---- 3. select on the list: thread t holds entries per t .. per t + per - 1 ----
+        const int per = (int(n_keep) + kThreads - 1) / kThreads;   // at most kPer
         uint32_t lk[kPer];
         int32_t lp[kPer];
         bool lv[kPer];
-        uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int idx = kPer * tid + j;
-            lv[j] = idx < n_keep;
-            lk[j] = lv[j] ? big[idx] : 0u;
-            lp[j] = lv[j] ? int32_t(big[kListCap + idx]) : 0;
-            if (lv[j]) {
-                kmin = min(kmin, lk[j]);
-                kmax = max(kmax, lk[j]);
-            }
+            const int idx = per * tid + j;
+            lv[j] = j < per && idx < int(n_keep);
+            const uint2 v = lv[j] ? list[idx] : make_uint2(0u, 0u);
+            lk[j] = v.x;
+            lp[j] = int32_t(v.y);
         }
-        kmin = wave_min(kmin);
-        kmax = wave_max(kmax);
-        if (lane == 0) {
-            atomicMin(&sh_mm[0], kmin);
-            atomicMax(&sh_mm[1], kmax);
-        }
-        __syncthreads();                 // the list is in registers; `big` is free again
-        uint32_t prefix = 0, mask = 0;
-        int remaining = k;               // how many of the entries matching `prefix` under `mask` to keep
+        // The k-th largest key lies in [lo_k, hi_k], initially [t_lo, kmax] (every list key).  A
+        // pass splits the interval into 4,096 bins of 2^sh keys, (key - lo_k) >> sh, so the bins
+        // cover it evenly whatever the float exponents, and keeps the bin that holds the k-th
+        // largest: sh drops by 12 a pass until the bin is a single key, or the bin is kept whole.
+        uint32_t lo_k = t_lo, hi_k = sh_kmax;
+        int remaining = k;               // how many of the entries in [lo_k, hi_k] to keep
         int pass = 0;
-        bool done = false;
-        if (sh_mm[0] == sh_mm[1]) {      // uniform: every entry has the same key
-            prefix = sh_mm[0];
-            mask = 0xffffffffu;
-            done = true;
-        } else {
-            // 12-bit first digit
-            uint32_t* h12 = big;
-            for (int i = tid; i < kBins1 * kCopies12; i += kThreads) h12[i] = 0;
-            if (tid == 0) {
-                sh_mm[2] = 0xffffffffu;
-                sh_mm[3] = 0u;
-            }
-            __syncthreads();
-            const int copy = tid & (kCopies12 - 1);
+        if (hi_k != lo_k) {              // uniform (equal: every entry has the same key)
+            int sh = max(0, 32 - __builtin_clz(hi_k - lo_k) - 12);
+            for (bool done = false; !done; ++pass) {         // uniform; at most 3 passes
+                uint32_t* h = hist[pass & 1];
+                // the other buffer was last read before the previous pass's selection barrier
+                if (pass >= 1)
+                    for (int i = tid; i < kBins1; i += kThreads) hist[(pass + 1) & 1][i] = 0;
 #pragma unroll
-            for (int j = 0; j < kPer; ++j)
-                if (lv[j]) atomicAdd(&h12[(lk[j] >> kShift1) * kCopies12 + copy], 1u);
-            __syncthreads();
-            uint32_t c[4];
-            int t = 0;
+                for (int j = 0; j < kPer; ++j)
+                    if (lv[j] && lk[j] >= lo_k && lk[j] <= hi_k) atomicAdd(&h[(lk[j] - lo_k) >> sh], 1u);
+                __syncthreads();
+                uint32_t c[4];
+                int t = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int dgt = kBins1 - 1 - 4 * tid - e;
-                c[e] = 0;
-#pragma unroll
-                for (int j = 0; j < kCopies12; ++j) c[e] += h12[dgt * kCopies12 + j];
-                t += int(c[e]);
-            }
-            int total;
-            int above = block_exclusive_scan(t, sh_scan[1], &total);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (above < remaining && above + int(c[e]) >= remaining) {
-                    sh_sel[0] = kBins1 - 1 - 4 * tid - e;
-                    sh_sel[1] = remaining - above;
-                    sh_sel[2] = int(c[e]);
+                for (int e = 0; e < 4; ++e) {
+                    c[e] = h[kBins1 - 1 - 4 * tid - e];
+                    t += int(c[e]);
                 }
-                above += int(c[e]);
-            }
-            __syncthreads();
-            prefix = uint32_t(sh_sel[0]) << kShift1;
-            mask = 0xfff00000u;
-            remaining = sh_sel[1];
-            done = sh_sel[2] == remaining;       // the whole bin is kept
-            __syncthreads();
-        }
-        // 8, 8 and 4 more bits over the entries still matching
-        for (int shift = 12; !done && shift >= -4; shift -= 8, ++pass) {
-            const int sh = shift > 0 ? shift : 0;
-            const uint32_t width_mask = shift > 0 ? 255u : 15u;
-            uint32_t* h = hist[pass & 1];
-            // the other buffer was last read before the previous pass's selection barrier
-            for (int i = tid; i < 256 * kCopies; i += kThreads) hist[(pass + 1) & 1][i] = 0;
-            const int copy = tid & (kCopies - 1);
-            uint32_t lo = 0xffffffffu, hi = 0u;
+                int total;
+                int above = block_exclusive_scan(t, sh_scan[pass & 1], &total);
 #pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-                if (lv[j] && (lk[j] & mask) == prefix) {
-                    atomicAdd(&h[((lk[j] >> sh) & width_mask) * kCopies + copy], 1u);
-                    lo = min(lo, lk[j]);
-                    hi = max(hi, lk[j]);
+                for (int e = 0; e < 4; ++e) {
+                    if (above < remaining && above + int(c[e]) >= remaining) {
+                        sh_sel[pass & 1][0] = kBins1 - 1 - 4 * tid - e;
+                        sh_sel[pass & 1][1] = remaining - above;
+                        sh_sel[pass & 1][2] = int(c[e]);
+                    }
+                    above += int(c[e]);
                 }
-            }
-            lo = wave_min(lo);
-            hi = wave_max(hi);
-            const int slot = 2 * ((pass + 1) & 1);   // sh_mm[0..1] held the whole list's range
-            if (lane == 0) {
-                atomicMin(&sh_mm[slot], lo);
-                atomicMax(&sh_mm[slot + 1], hi);
-            }
-            if (tid == 0) {
-                sh_mm[2 * (pass & 1)] = 0xffffffffu;
-                sh_mm[2 * (pass & 1) + 1] = 0u;
-            }
-            __syncthreads();
-            if (sh_mm[slot] == sh_mm[slot + 1]) {      // uniform
-                prefix = sh_mm[slot];
-                mask = 0xffffffffu;
-                break;
-            }
-            int cb = 0;
-            if (tid < 256) {
-                const int dgt = 255 - tid;
+                __syncthreads();
+                lo_k += uint32_t(sh_sel[pass & 1][0]) << sh;
+                hi_k = uint32_t(min(uint64_t(hi_k), uint64_t(lo_k) + ((uint64_t(1) << sh) - 1)));
+                remaining = sh_sel[pass & 1][1];
+                const int in_bin = sh_sel[pass & 1][2];
+                // the whole bin is kept, or the bin is one key
+                done = in_bin == remaining || sh == 0;
+                if (!done && in_bin >= kTied) {          // uniform
+                    // A bin of dozens of entries is often one key repeated (integer-valued scores,
+                    // ties): its range decides that in one reduction, where a histogram pass would
+                    // queue the entries on one LDS address.
+                    uint32_t blo = 0xffffffffu, bhi = 0u;
 #pragma unroll
-                for (int j = 0; j < kCopies; ++j) cb += h[dgt * kCopies + ((j + tid) & (kCopies - 1))];
+                    for (int j = 0; j < kPer; ++j) {
+                        if (lv[j] && lk[j] >= lo_k && lk[j] <= hi_k) {
+                            blo = min(blo, lk[j]);
+                            bhi = max(bhi, lk[j]);
+                        }
+                    }
+                    blo = wave_min(blo);
+                    bhi = wave_max(bhi);
+                    uint32_t* mm = sh_mm + 2 * pass;   // each pass's slots are used once
+                    if (lane == 0) {
+                        atomicMin(&mm[0], blo);
+                        atomicMax(&mm[1], bhi);
+                    }
+                    __syncthreads();
+                    if (mm[0] == mm[1]) {                               // uniform
+                        lo_k = hi_k = mm[0];
+                        done = true;
+                    }
+                }
+                sh = sh >= 12 ? sh - 12 : 0;
             }
-            int total;
-            const int above = block_exclusive_scan(cb, sh_scan[pass & 1], &total);
-            if (tid < 256 && above < remaining && above + cb >= remaining) {
-                sh_sel[0] = 255 - tid;
-                sh_sel[1] = remaining - above;
-                sh_sel[2] = cb;
-            }
-            __syncthreads();
-            const uint32_t dgt = uint32_t(sh_sel[0]);
-            remaining = sh_sel[1];
-            const int bin_count = sh_sel[2];
-            __syncthreads();
-            prefix |= dgt << sh;
-            mask |= width_mask << sh;
-            if (bin_count == remaining) break;
         }
-        // kept entries in list order: above the threshold, or equal to it and among the first
-        // `remaining` equal ones; packed (above << 16 | equal) counts, both below 2^16 here
+        // kept entries in list order: above hi_k, or in [lo_k, hi_k] and among the first
+        // `remaining` there; packed (above << 16 | in) counts, both below 2^16 here
         uint32_t cc = 0;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const uint32_t m = lk[j] & mask;
-            cc += (lv[j] && m > prefix) ? 0x10000u : 0u;
-            cc += (lv[j] && m == prefix) ? 1u : 0u;
+            cc += (lv[j] && lk[j] > hi_k) ? 0x10000u : 0u;
+            cc += (lv[j] && lk[j] >= lo_k && lk[j] <= hi_k) ? 1u : 0u;
         }
         int total;
         const uint32_t cpre = uint32_t(block_exclusive_scan(int(cc), sh_scan[pass & 1], &total));
@@ -384,9 +360,8 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
         int off = gt + min(eq, remaining);
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const uint32_t m = lk[j] & mask;
-            bool take = lv[j] && m > prefix;
-            if (lv[j] && m == prefix) take = eq++ < remaining;
+            bool take = lv[j] && lk[j] > hi_k;
+            if (lv[j] && lk[j] >= lo_k && lk[j] <= hi_k) take = eq++ < remaining;
             if (take && off < k) o[off++] = lp[j];
         }
         return;
@@ -444,14 +419,14 @@ __global__ void __launch_bounds__(kThreads) topk_radix_kernel(const float* __res
         int total;
         const int above = block_exclusive_scan(c, sh_scan[pass & 1], &total);  // count with a larger digit
         if (tid < 256 && above < remaining && above + c >= remaining) {
-            sh_sel[0] = 255 - tid;
-            sh_sel[1] = remaining - above;
-            sh_sel[2] = c;
+            sh_sel[0][0] = 255 - tid;
+            sh_sel[0][1] = remaining - above;
+            sh_sel[0][2] = c;
         }
         __syncthreads();
-        const uint32_t dgt = sh_sel[0];
-        remaining = sh_sel[1];
-        const int in_bin = sh_sel[2];
+        const uint32_t dgt = sh_sel[0][0];
+        remaining = sh_sel[0][1];
+        const int in_bin = sh_sel[0][2];
         __syncthreads();
         prefix |= dgt << shift;
         mask |= 255u << shift;

@@ -301,6 +301,55 @@ def test_topk_random_floats(tsa):
         assert np.array_equal(got[b], otopk.select_padded(s[b, :lens[b]], k)), f"row {b}"
 
 
+@pytest.mark.parametrize("max_len", [901, 2000, 4000, 8000, 12001, 16000, 24000, 32768, 48000, 65536])
+def test_topk_every_launch_shape(tsa, max_len):
+    """One max length per scores-per-thread class of the top-k launch (1 .. 64 per thread):
+    rows of floats with repeated values, integer-valued rows with many ties, and a row of one
+    repeated value; lengths drawn up to max_len (two odd maxima take the scalar score loads).
+    Bit-exact against the oracle's selection."""
+    rng = np.random.default_rng(max_len)
+    B, k = 8, 512
+    s = rng.standard_normal((B, max_len)).astype(np.float32)
+    s[:, ::5] = np.round(s[:, ::5], 1)
+    s[2:5] = np.maximum(0, np.round(rng.normal(0, 75, size=(3, max_len)))).astype(np.float32)
+    s[5] = 3.0
+    lens = rng.integers(1, max_len + 1, size=B).astype(np.int32)
+    lens[0] = max_len
+    p = tsa.decode_params(B, 8, k, max_len, 1.0)
+    out = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    print(f"[topk] max_len {max_len}", flush=True)
+    tsa.topk(p, torch.from_numpy(s).cuda(), torch.from_numpy(lens).cuda(), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(got[b], otopk.select_padded(s[b, :lens[b]], k)), f"row {b}, len {lens[b]}"
+
+
+def test_topk_signed_zeros_and_nans(tsa):
+    """Scores compared as floats, as the oracle does: -0 equals +0 (ties by position) and a NaN
+    ranks below every number (NaNs by position).  Row 0 keeps only numbers (the list path),
+    row 1 needs some of its NaNs (the general path), row 2 is zeros of both signs only."""
+    rng = np.random.default_rng(21)
+    L, k = 6000, 512
+    s = np.zeros((3, L), dtype=np.float32)
+    s[0] = np.round(rng.normal(0, 0.2, size=L))            # mostly zeros: the k-th score is 0
+    s[0, rng.choice(L, 300, replace=False)] = np.nan
+    s[0, ::3] = -s[0, ::3]                                 # -0 among the zeros
+    s[1] = np.nan
+    s[1, rng.choice(L, 400, replace=False)] = -0.0
+    s[1, rng.choice(L, 50, replace=False)] = 1.5
+    s[2] = np.where(rng.random(L) < 0.5, -0.0, 0.0)
+    lens = np.array([L, L, L], dtype=np.int32)
+    p = tsa.decode_params(3, 8, k, L, 1.0)
+    out = torch.empty((3, k), dtype=torch.int32, device="cuda")
+    tsa.topk(p, torch.from_numpy(s).cuda(), torch.from_numpy(lens).cuda(), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.signbit(s[0][s[0] == 0]).any() and np.signbit(s[2]).any()
+    for b in range(3):
+        assert np.array_equal(got[b], otopk.select_padded(s[b], k)), f"row {b}"
+
+
 def test_gather_given_positions(tsa):
     """Attention over caller-given positions, with invalid entries to skip."""
     st = staged("tiny_b5")

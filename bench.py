@@ -44,7 +44,8 @@ def _src_hash(name: str) -> str:
         code += [ln.rstrip() for ln in open(os.path.join(csrc, f), encoding="utf-8")
                  if ln.strip() and not ln.lstrip().startswith("//")]
     from top_sparse_attention_amd import build as _build
-    code.append(" ".join(_build.FLAGS))
+    # the flags, without the include paths: those name where the tree sits, not what is built
+    code.append(" ".join(f for f in _build.FLAGS if not f.startswith("-I")))
     return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 

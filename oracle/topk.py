@@ -10,7 +10,10 @@ scores the lower position wins.  The result is returned as ascending
 positions, so two correct selections compare equal element by element.
 
 Method: a full sort by (score descending, position ascending) and the first k
-entries, i.e. the definition itself.
+entries, i.e. the definition itself.  Scores compare as floats: -0 equals +0
+(a tie, decided by position), and numpy's sort puts a NaN after every number,
+so a NaN ranks last (NaNs among themselves by position).  Indexer scores have
+neither; the reading matters only for scores a caller passes in.
 """
 from __future__ import annotations
 

@@ -160,3 +160,15 @@ def test_relu_zero_class_fills_by_position():
 def test_padded_layout():
     out = topk.select_padded(np.array([3, 1, 2]), 5)
     assert out.dtype == np.int32 and out.tolist() == [0, 1, 2, -1, -1]
+
+
+def test_signed_zeros_tie_and_nan_ranks_last():
+    """Worked by hand.  Scores by position: NaN, 1, -0, +0, NaN, -0, 2, NaN, -1.  Descending:
+    2 (pos 6), 1 (pos 1), then the three zeros of either sign as one tie class by position
+    (2, 3, 5), then -1 (pos 8), then the NaNs by position (0, 4, 7)."""
+    s = np.array([np.nan, 1.0, -0.0, 0.0, np.nan, -0.0, 2.0, np.nan, -1.0], dtype=np.float32)
+    assert topk.select(s, 3).tolist() == [1, 2, 6]          # 2, 1 and the first zero (pos 2)
+    assert topk.select(s, 5).tolist() == [1, 2, 3, 5, 6]
+    assert topk.select(s, 6).tolist() == [1, 2, 3, 5, 6, 8]
+    assert topk.select(s, 7).tolist() == [0, 1, 2, 3, 5, 6, 8]
+    assert topk.select(s, 8).tolist() == [0, 1, 2, 3, 4, 5, 6, 8]

@@ -328,7 +328,8 @@ def test_topk_every_launch_shape(tsa, max_len):
 def test_topk_signed_zeros_and_nans(tsa):
     """Scores compared as floats, as the oracle does: -0 equals +0 (ties by position) and a NaN
     ranks below every number (NaNs by position).  Row 0 keeps only numbers (the list path),
-    row 1 needs some of its NaNs (the general path), row 2 is zeros of both signs only."""
+    row 1 needs some of its NaNs (the general path), row 2 is zeros of both signs and a few
+    denormals of either sign (kept apart from the zeros: no flush to zero)."""
     rng = np.random.default_rng(21)
     L, k = 6000, 512
     s = np.zeros((3, L), dtype=np.float32)
@@ -339,6 +340,8 @@ def test_topk_signed_zeros_and_nans(tsa):
     s[1, rng.choice(L, 400, replace=False)] = -0.0
     s[1, rng.choice(L, 50, replace=False)] = 1.5
     s[2] = np.where(rng.random(L) < 0.5, -0.0, 0.0)
+    s[2, rng.choice(L, 40, replace=False)] = np.float32(1e-40)    # denormals rank above the zeros
+    s[2, rng.choice(L, 40, replace=False)] = np.float32(-1e-40)   # ... and below them
     lens = np.array([L, L, L], dtype=np.int32)
     p = tsa.decode_params(3, 8, k, L, 1.0)
     out = torch.empty((3, k), dtype=torch.int32, device="cuda")

@@ -193,7 +193,8 @@ tsa_status tsa_indexer_scores(tsa_kv_pool* pool, int32_t layer, const tsa_decode
                               void* stream);
 
 /* Top-k of precomputed scores: fp32 [B][ld]; topk_dev: int32 [B][top_k], ascending
- * positions, -1 after the min(seq_len, top_k) selected ones.  NaN ranks above +inf. */
+ * positions, -1 after the min(seq_len, top_k) selected ones.  Scores compare as floats: -0
+ * equals +0, equal scores go to the lowest position, and a NaN ranks below every number. */
 tsa_status tsa_topk(const tsa_decode_params* p, const float* scores_dev, int32_t ld,
                     const int32_t* seq_lens_dev, int32_t* topk_dev, void* stream);
 

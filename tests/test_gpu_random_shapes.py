@@ -1,0 +1,139 @@
+"""The whole decode step on seeded random shapes against the oracle.
+
+Each seed draws one configuration: the latent layout (576-dim rows whose first 512 dims are the
+values, one KV head, 8 to 128 query heads) or a grouped-query layout (head dims 64 to 256, some
+with values aliasing the keys, 1 to 32 query heads per KV head), a page size from 1 to 128, an
+indexer of 32 to 128 dims with 1 to 64 heads, a ragged batch of up to 9 requests (lengths from 0
+to 5,000, page boundaries included) and a top-k from 1 to 2,048.  So the draws reach every
+attention kernel (latent and grouped-query matrix-core kernels, the vector-ALU kernel), both
+indexer kernels and both top-k paths.  Indexer scores and top-k sets must equal the oracle's bit
+for bit and every request's attention must be within the 2e-3 normwise bar.
+"""
+import dataclasses
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import decode, sdpa
+
+pytestmark = pytest.mark.gpu
+
+ATOL_REL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def tsa():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import top_sparse_attention_amd as m
+    m.load()
+    return m
+
+
+def _draw(seed):
+    """One configuration: (base workload, field replacements, stage keyword arguments)."""
+    rng = np.random.default_rng(1000 + seed)
+    if rng.random() < 0.4:
+        base = "mla_b64_32k"
+        wrep = {"num_q_heads": int(rng.choice([8, 16, 48, 64, 128]))}
+    else:
+        base = "gqa_b32_8k"
+        dk, dv, alias = [(64, 64, False), (128, 128, False), (192, 128, False), (256, 256, False),
+                         (96, 96, False), (128, 64, True)][int(rng.integers(6))]
+        hkv = int(rng.choice([1, 2, 4, 8]))
+        g = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        wrep = {"head_dim_k": dk, "head_dim_v": dv, "v_from_k": alias, "num_kv_heads": hkv,
+                "num_q_heads": hkv * g}
+    page = int(rng.choice([1, 8, 16, 48, 64, 128]))
+    wrep["index_dim"] = int(rng.choice([32, 64, 128]))
+    heads = int(rng.choice([1, 2, 4, 16, 64]))
+    if page < 16:                       # the register indexer kernel takes up to 8 heads
+        heads = min(heads, 8)
+    wrep["top_k"] = int(rng.choice([1, 3, 64, 100, 512, 2048]))
+    B = int(rng.integers(1, 10))
+    lens = rng.integers(0, 5001, size=B)
+    edges = [0, 1, page - 1, page, page + 1, 2 * page, wrep["top_k"], wrep["top_k"] + 1]
+    for i in range(B):
+        if rng.random() < 0.3:
+            lens[i] = max(0, int(rng.choice(edges)))
+    return base, wrep, dict(lens=lens.astype(np.int32), page_size=page, index_heads=heads)
+
+
+# 48 draws by default; RANDOM_SHAPES=N runs more of the same sequence
+@pytest.mark.parametrize("seed", range(int(os.environ.get("RANDOM_SHAPES", "48"))))
+def test_random_shape_step_matches_oracle(tsa, seed):
+    from top_sparse_attention_amd import workload
+    base, wrep, kw = _draw(seed)
+    print(f"[random shape {seed}] {base} {wrep} page {kw['page_size']} index heads "
+          f"{kw['index_heads']} lens {kw['lens'].tolist()}", flush=True)
+    w = dataclasses.replace(synth.get(base), **wrep)
+    st = workload.stage(w, seed=seed, **kw)
+    B = len(st.lens)
+    ld = max(64, -(-st.params.max_len // 64) * 64)
+    sc = torch.full((B, ld), float("nan"), dtype=torch.float32, device="cuda")
+    tsa.indexer_scores(st.pool, 0, st.params, st.qidx, st.widx, st.table_dev, st.lens_dev, sc)
+    st.step(append=False)
+    torch.cuda.synchronize()
+    scores = sc.cpu().numpy()
+    topk = st.topk.cpu().numpy()
+    out = st.out.double().cpu().numpy()
+    for b in range(B):
+        L = int(st.lens[b])
+        if L == 0:                      # nothing to score or attend: no selection, zero output
+            assert (topk[b] == -1).all() and not out[b].any(), f"empty request {b}"
+            continue
+        kidx, kk, vv = synth.request_tokens(w, st.seed, b, L)
+        s_ref, sel_ref, o_ref = decode.request_step(
+            st.q_np[b], st.qidx_np[b], st.widx_np, kidx, kk, vv, w.top_k, w.sm_scale,
+            v_from_k_dims=w.head_dim_v if w.v_from_k else 0)
+        assert np.array_equal(scores[b, :L].astype(np.float64), np.asarray(s_ref, np.float64)), \
+            f"scores differ, request {b} (len {L})"
+        exp = np.full(w.top_k, -1, dtype=np.int32)
+        exp[:len(sel_ref)] = sel_ref
+        assert np.array_equal(topk[b], exp), f"top-k differs, request {b} (len {L})"
+        err = sdpa.normwise_rel_err(out[b], o_ref)
+        assert err < ATOL_REL, f"attention error {err} on request {b} (len {L})"
+
+
+@pytest.mark.parametrize("base,page", [("mla_b64_32k", 64), ("mla_b64_32k", 48), ("gqa_b32_8k", 8),
+                                       ("tiny_b5", 16)])
+def test_all_empty_batch_every_entry_point(tsa, base, page):
+    """A batch whose requests are all empty (every length 0, so the longest is 0): each step
+    entry point runs, selects nothing and writes zero outputs."""
+    from top_sparse_attention_amd import workload
+    lens = np.zeros(3, dtype=np.int32)
+    print(f"[empty batch] {base} page {page}", flush=True)
+    st = workload.stage(synth.get(base), seed=0, lens=lens, page_size=page)
+    B = len(lens)
+    w = st.w
+    assert st.params.max_len == 0
+
+    def fresh():
+        st.out.fill_(float("nan"))
+        st.topk.fill_(7)
+    fresh()
+    tsa.sparse_decode_attn(st.pool, 0, st.params, st.q, st.qidx, st.widx, st.table_dev, st.lens_dev,
+                           st.out, st.workspace, topk_out=st.topk)
+    torch.cuda.synchronize()
+    assert (st.topk.cpu() == -1).all() and not st.out.cpu().double().numpy().any()
+    fresh()
+    # new-token rows of the right shape (an empty request appends nothing)
+    k_new = torch.zeros((B, w.num_kv_heads * w.head_dim_k), dtype=torch.int16, device="cuda")
+    v_new = None if w.v_from_k else torch.zeros((B, w.num_kv_heads * w.head_dim_v), dtype=torch.int16,
+                                                device="cuda")
+    i_new = torch.zeros((B, w.index_dim), dtype=torch.int16, device="cuda")
+    tsa.decode_step(st.pool, 0, st.params, k_new, v_new, i_new, st.q, st.qidx, st.widx,
+                    st.table_dev, st.lens_dev, st.out, st.workspace, topk_out=st.topk)
+    torch.cuda.synchronize()
+    assert (st.topk.cpu() == -1).all() and not st.out.cpu().double().numpy().any()
+    fresh()
+    tsa.indexer_topk(st.pool, 0, st.params, st.qidx, st.widx, st.table_dev, st.lens_dev, st.topk,
+                     st.workspace)
+    tsa.sparse_attn_gather(st.pool, 0, st.params, st.q, st.topk, st.table_dev, st.lens_dev, st.out,
+                           st.workspace)
+    torch.cuda.synchronize()
+    assert (st.topk.cpu() == -1).all() and not st.out.cpu().double().numpy().any()
+    assert st.out.shape[0] == B and st.topk.shape == (B, w.top_k)

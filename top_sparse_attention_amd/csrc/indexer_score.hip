@@ -448,7 +448,9 @@ hipError_t launch_lds(const tsa_kv_pool& pool, int layer, const tsa_decode_param
     int tpw = int((total + 4095) / 4096);
     tpw = std::max(kUnit * 4, std::min(tpw, kMaxTpw));
     tpw = (tpw + kUnit - 1) / kUnit * kUnit;
-    dim3 grid((p.max_len + 4 * tpw - 1) / (4 * tpw), p.batch + (fused.k_src ? 1 : 0));
+    // at least one column of workgroups: a batch whose requests are all empty still launches
+    // (every scoring workgroup exits at once; the append row, if any, writes nothing)
+    dim3 grid(std::max(1, (p.max_len + 4 * tpw - 1) / (4 * tpw)), p.batch + (fused.k_src ? 1 : 0));
     const uint16_t* kpool = static_cast<const uint16_t*>(pool.idx) + int64_t(layer) * pool.slots() * D;
     const bool aligned = shift >= 0 && d.page_size % kUnit == 0;
     if (aligned)
@@ -484,7 +486,7 @@ hipError_t launch_lpt(const tsa_kv_pool& pool, int layer, const tsa_decode_param
                       hipStream_t s) {
     const tsa_pool_desc& d = pool.d;
     const int tok_per_block = (kThreads / LPT) * kUnroll * kRounds;
-    dim3 grid((p.max_len + tok_per_block - 1) / tok_per_block, p.batch);
+    dim3 grid(std::max(1, (p.max_len + tok_per_block - 1) / tok_per_block), p.batch);
     int shift = -1;
     if ((d.page_size & (d.page_size - 1)) == 0) {
         shift = 0;

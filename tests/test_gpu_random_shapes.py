@@ -137,3 +137,51 @@ def test_all_empty_batch_every_entry_point(tsa, base, page):
     torch.cuda.synchronize()
     assert (st.topk.cpu() == -1).all() and not st.out.cpu().double().numpy().any()
     assert st.out.shape[0] == B and st.topk.shape == (B, w.top_k)
+
+
+@pytest.mark.parametrize("seed", range(int(os.environ.get("RANDOM_SHAPES", "48"))))
+def test_random_shape_decode_step_matches_oracle(tsa, seed):
+    """tsa_decode_step on the same draws, short ones made shorter so that some take the one-launch
+    step: each request's newest token is written inside the step (scoring launch, separate append
+    or one-launch kernel) and the result must match the oracle over all L tokens."""
+    from top_sparse_attention_amd import workload
+    base, wrep, kw = _draw(seed)
+    if seed % 3 == 0:                   # short contexts, few rows: the one-launch step's range
+        kw["lens"] = np.minimum(kw["lens"], 900).astype(np.int32)
+        wrep["top_k"] = min(wrep["top_k"], 64)
+    print(f"[random step {seed}] {base} {wrep} page {kw['page_size']} index heads "
+          f"{kw['index_heads']} lens {kw['lens'].tolist()}", flush=True)
+    w = dataclasses.replace(synth.get(base), **wrep)
+    st = workload.stage(w, seed=seed, **kw)
+    B = len(st.lens)
+    # one new-row per request; empty requests append nothing, so theirs stay zero
+    k_new = torch.zeros((B, w.num_kv_heads * w.head_dim_k), dtype=torch.int16, device="cuda")
+    v_new = None if w.v_from_k else torch.zeros((B, w.num_kv_heads * w.head_dim_v), dtype=torch.int16,
+                                                device="cuda")
+    i_new = torch.zeros((B, w.index_dim), dtype=torch.int16, device="cuda")
+    if st.new_req is not None:
+        nz = st.new_req.long()
+        k_new[nz] = st.new_k.view(torch.int16).reshape(len(nz), -1)
+        if v_new is not None:
+            v_new[nz] = st.new_v.view(torch.int16).reshape(len(nz), -1)
+        i_new[nz] = st.new_idx.view(torch.int16).reshape(len(nz), -1)
+    st.out.fill_(float("nan"))
+    tsa.decode_step(st.pool, 0, st.params, k_new, v_new, i_new, st.q, st.qidx, st.widx,
+                    st.table_dev, st.lens_dev, st.out, st.workspace, topk_out=st.topk)
+    torch.cuda.synchronize()
+    topk = st.topk.cpu().numpy()
+    out = st.out.double().cpu().numpy()
+    for b in range(B):
+        L = int(st.lens[b])
+        if L == 0:
+            assert (topk[b] == -1).all() and not out[b].any(), f"empty request {b}"
+            continue
+        kidx, kk, vv = synth.request_tokens(w, st.seed, b, L)
+        _, sel_ref, o_ref = decode.request_step(
+            st.q_np[b], st.qidx_np[b], st.widx_np, kidx, kk, vv, w.top_k, w.sm_scale,
+            v_from_k_dims=w.head_dim_v if w.v_from_k else 0)
+        exp = np.full(w.top_k, -1, dtype=np.int32)
+        exp[:len(sel_ref)] = sel_ref
+        assert np.array_equal(topk[b], exp), f"top-k differs, request {b} (len {L})"
+        err = sdpa.normwise_rel_err(out[b], o_ref)
+        assert err < ATOL_REL, f"attention error {err} on request {b} (len {L})"

@@ -370,3 +370,58 @@ def test_latent_selection_beyond_64_splits_leaves_the_matrix_core_kernel():
     n = 64 * 64
     partial = (2 * n + n * 512) * 4
     assert 0 < ws <= scores + topk + partial + 3 * 256
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_tables_build_grow_release_match_oracle(seed):
+    """Seeded random batches through build, grow and release: tables, page counts, saved pages
+    and refcounts equal the oracle's; a pool too small for a build or a grow is refused by both,
+    with nothing changed; releasing everything returns every page."""
+    rng = np.random.default_rng(seed)
+    P = int(rng.choice([1, 2, 8, 16, 48, 64, 128]))
+    n = int(rng.integers(1, 13))
+    lens = rng.integers(0, 1500, size=n)
+    grp = np.full(n, -1, dtype=np.int32)
+    plen = []
+    for g in range(int(rng.integers(0, 4))):
+        members = rng.choice(n, size=int(rng.integers(1, n + 1)), replace=False)
+        members = [m for m in members if grp[m] < 0]
+        if not members:
+            continue
+        gi = len(plen)
+        grp[members] = gi
+        plen.append(int(rng.integers(0, int(lens[members].min()) + 1)))
+    need = sum(-(-int(L) // P) for L in lens)
+    N = max(1, need + int(rng.integers(-3, 40)))
+    fo = rng.permutation(N).astype(np.int32)
+    maxp = max(1, -(-2000 // P))
+    pool = _pool(N, P, free_order=fo)
+    args = (grp, plen) if plen else (None, None)
+    try:
+        ref = paging.build_page_tables(lens, P, fo, *args, max_pages=maxp) if plen else \
+            paging.build_page_tables(lens, P, fo, max_pages=maxp)
+    except MemoryError:
+        with pytest.raises(tsa.TsaError) as e:
+            pool.build_tables(lens, maxp, *args) if plen else pool.build_tables(lens, maxp)
+        assert e.value.status == _lib.TSA_ERR_OUT_OF_PAGES and pool.usage() == (N, 0)
+        return
+    table, num, saved = pool.build_tables(lens, maxp, *args) if plen else pool.build_tables(lens, maxp)
+    assert np.array_equal(table, ref["table"]) and np.array_equal(num, ref["num_pages"])
+    assert saved == ref["saved"] and pool.usage()[1] == ref["pages_in_use"]
+    for p in np.unique(table[table >= 0]):
+        assert pool.refcount(int(p)) == ref["refcount"][p]
+    # grow: requests without shared pages may lengthen (a write into a shared page is refused)
+    new = np.array([L + (int(rng.integers(0, 300)) if grp[i] < 0 else 0) for i, L in enumerate(lens)])
+    try:
+        g = paging.grow_page_tables(ref["table"], ref["num_pages"], new, P, ref["free"])
+    except MemoryError:
+        before = (table.copy(), num.copy(), pool.usage())
+        with pytest.raises(tsa.TsaError) as e:
+            pool.grow_tables(table, num, new)
+        assert e.value.status == _lib.TSA_ERR_OUT_OF_PAGES
+        assert np.array_equal(table, before[0]) and np.array_equal(num, before[1]) and pool.usage() == before[2]
+    else:
+        pool.grow_tables(table, num, new)
+        assert np.array_equal(table, g["table"]) and np.array_equal(num, g["num_pages"])
+    pool.release_tables(table, num)
+    assert pool.usage() == (N, 0)

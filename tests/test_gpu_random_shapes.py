@@ -185,3 +185,70 @@ def test_random_shape_decode_step_matches_oracle(tsa, seed):
         assert np.array_equal(topk[b], exp), f"top-k differs, request {b} (len {L})"
         err = sdpa.normwise_rel_err(out[b], o_ref)
         assert err < ATOL_REL, f"attention error {err} on request {b} (len {L})"
+
+
+@pytest.mark.parametrize("seed", range(int(os.environ.get("RANDOM_SHAPES", "48")) // 2))
+def test_random_appends_land_where_the_oracle_says(tsa, seed):
+    """Seeded random tsa_kv_append calls (several layers, ragged tables, page sizes 1-128, values
+    aliased or separate, with or without indexer rows): every row lands in the physical slot the
+    oracle's table gives, every other byte of the pool is unchanged, and each refused token
+    (request or position out of range, position past the request's pages) is counted once."""
+    from oracle import paging
+    rng = np.random.default_rng(500 + seed)
+    P = int(rng.choice([1, 8, 16, 48, 64, 128]))
+    NL = int(rng.integers(1, 4))
+    hkv = int(rng.choice([1, 2, 4]))
+    dk = int(rng.choice([64, 128, 576]))
+    alias = dk == 576 or bool(rng.random() < 0.3)
+    dv = 512 if dk == 576 else (dk if not alias else dk // 2)
+    D = int(rng.choice([0, 32, 128]))
+    n = int(rng.integers(1, 8))
+    lens = rng.integers(0, 800, size=n)
+    need = sum(-(-int(L) // P) for L in lens)
+    N = need + int(rng.integers(1, 20))
+    fo = rng.permutation(N).astype(np.int32)
+    maxp = max(1, -(-900 // P))
+    pool = tsa.KvPool(N, P, hkv, dk, dv, num_layers=NL, v_from_k=alias, index_dim=D, free_order=fo)
+    table, num, _ = pool.build_tables(lens, maxp)
+    ref = paging.build_page_tables(lens, P, fo, max_pages=maxp)
+    assert np.array_equal(table, ref["table"])
+    table_dev = torch.from_numpy(table).cuda()
+    slots = N * P
+    regions = [(pool.k, hkv * dk)] + ([] if pool.v is None else [(pool.v, hkv * dv)]) + \
+              ([] if pool.idx is None else [(pool.idx, D)])
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    for t, _ in regions:
+        t.view(torch.int16).copy_(torch.randint(-30000, 30000, t.shape, generator=g, device="cuda",
+                                                dtype=torch.int16))
+    expect = [t.view(torch.int16).cpu().numpy().reshape(NL * slots, width).copy() for t, width in regions]
+    for layer in range(NL):
+        # distinct valid tokens, plus refused ones of every kind
+        valid = [(r, p) for r in range(n) for p in range(int(num[r]) * P)]
+        pick = [valid[i] for i in rng.choice(len(valid), size=min(len(valid), 60), replace=False)] if valid else []
+        refused = [(n + 1, 0), (-1, 0), (0, -5), (0, maxp * P + 3)]
+        refused += [(r, int(num[r]) * P + int(rng.integers(0, P))) for r in range(n) if num[r] < maxp][:3]
+        items = pick + refused
+        order = rng.permutation(len(items))
+        req = np.array([items[i][0] for i in order], dtype=np.int32)
+        pos = np.array([items[i][1] for i in order], dtype=np.int32)
+        M = len(req)
+        rows = [rng.integers(-30000, 30000, size=(M, width)).astype(np.int16) for _, width in regions]
+        bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+        print(f"[random append {seed}] layer {layer} P {P} hkv {hkv} dk {dk} dv {dv} alias {alias} "
+              f"D {D} tokens {M} refused {len(refused)}", flush=True)
+        src = [torch.from_numpy(x).cuda() for x in rows]
+        k_src = src[0]
+        v_src = src[1] if pool.v is not None else None
+        i_src = src[-1] if pool.idx is not None else None
+        pool.append(layer, torch.from_numpy(req).cuda(), torch.from_numpy(pos).cuda(), table_dev, n,
+                    k_src, v_src, i_src, bad_dev=bad)
+        torch.cuda.synchronize()
+        for j in range(M):
+            r, p = int(req[j]), int(pos[j])
+            if 0 <= r < n and p >= 0 and p // P < maxp and table[r, p // P] >= 0:
+                s = layer * slots + paging.physical_slot(table, r, p, P)
+                for e, x in zip(expect, rows):
+                    e[s] = x[j]
+        assert int(bad.item()) == len(refused)
+        for (t, width), e in zip(regions, expect):
+            assert np.array_equal(t.view(torch.int16).cpu().numpy().reshape(NL * slots, width), e)

@@ -425,3 +425,64 @@ def test_random_tables_build_grow_release_match_oracle(seed):
         assert np.array_equal(table, g["table"]) and np.array_equal(num, g["num_pages"])
     pool.release_tables(table, num)
     assert pool.usage() == (N, 0)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_lru_tier_matches_oracle(seed):
+    """Seeded random tier runs: page or token units, 1-4 layers, 1-5 requests, capacities from
+    tight to roomy, a random preload, positions with -1 padding, and tags released in random
+    order while others stay in flight.  After every plan the slot table and the hit, miss and
+    eviction counts equal the oracle's; a plan the oracle cannot complete (every slot it would
+    need is pinned) is refused by the library with nothing changed."""
+    import copy
+    from oracle import lru
+    rng = np.random.default_rng(900 + seed)
+    P = int(rng.choice([1, 16, 64]))
+    L, R = int(rng.integers(1, 5)), int(rng.integers(1, 6))
+    NPR = int(rng.integers(4, 65)) if P > 1 else int(rng.integers(64, 1025))
+    keys = L * R * NPR
+    capacity = int(rng.integers(max(2, keys // 20), keys + 10))
+    cache = _pool(capacity, P, kv_heads=1, dk=64, dv=64)
+    tier = tsa.LruTier(cache, L, R, NPR)
+    oc = lru.LRUCache(capacity)
+    pre = rng.choice(keys, size=int(rng.integers(0, min(keys, capacity) + 1)), replace=False).astype(np.int64)
+    tier.preload(pre)
+    oc.preload(pre.tolist())
+    held, g, refused = [], 0, 0
+    for step in range(int(rng.integers(3, 8))):
+        for layer in range(L):
+            k = int(rng.integers(1, min(NPR * P, 300) + 1))
+            pos = np.full((R, k), -1, dtype=np.int32)
+            for r in range(R):
+                m = int(rng.integers(0, k + 1))
+                pos[r, :m] = np.sort(rng.choice(NPR * P, size=min(m, NPR * P), replace=False))[:m]
+            saved = copy.deepcopy(oc)
+            try:
+                ref = lru.plan_layer(oc, layer, R, NPR, pos, P, g)
+            except MemoryError:
+                oc = saved
+                before = tier.stats()
+                with pytest.raises(tsa.TsaError) as e:
+                    tier.plan(layer, g, pos)
+                assert e.value.status == _lib.TSA_ERR_CAPACITY and tier.stats() == before
+                refused += 1
+                for tag in held:                          # free everything and go on
+                    tier.release(tag)
+                    oc.release(tag)
+                held = []
+            else:
+                table, _ = tier.plan(layer, g, pos)
+                assert np.array_equal(table, ref), (seed, step, layer)
+                held.append(g)
+            g += 1
+            st = tier.stats()
+            assert (st["hits"], st["misses"], st["evictions"]) == (oc.hits, oc.misses, oc.evictions)
+            # release a random subset of the tags in flight, in random order
+            if held and rng.random() < 0.7:
+                chosen = [int(i) for i in rng.choice(len(held), size=int(rng.integers(1, len(held) + 1)),
+                                                     replace=False)]
+                for i in sorted(chosen, reverse=bool(rng.random() < 0.5)):
+                    tier.release(held[i])
+                    oc.release(held[i])
+                held = [t for j, t in enumerate(held) if j not in chosen]
+    assert refused or oc.hits + oc.misses > 0

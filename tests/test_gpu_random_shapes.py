@@ -252,3 +252,63 @@ def test_random_appends_land_where_the_oracle_says(tsa, seed):
         assert int(bad.item()) == len(refused)
         for (t, width), e in zip(regions, expect):
             assert np.array_equal(t.view(torch.int16).cpu().numpy().reshape(NL * slots, width), e)
+
+
+@pytest.mark.parametrize("seed", range(int(os.environ.get("RANDOM_SHAPES", "48")) // 3))
+def test_random_tier_fetch_copies_the_host_rows(tsa, seed):
+    """Seeded random tier runs on the GPU (page or token unit, random shapes and capacities,
+    tags released in random order): after each plan and fetch, the device slot table equals the
+    plan's, and every touched page's cache slot holds exactly that page's host K and V rows."""
+    rng = np.random.default_rng(1300 + seed)
+    P = int(rng.choice([1, 16, 64]))
+    hkv, d = int(rng.choice([1, 2])), int(rng.choice([64, 128]))
+    L, R = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+    NPR = int(rng.integers(4, 41)) if P > 1 else int(rng.integers(64, 513))
+    keys = L * R * NPR
+    # at least one layer's pages, so that a plan fits once nothing else is pinned; below the
+    # whole set, so that layers and held tags make evictions
+    capacity = int(rng.integers(max(8, R * NPR), max(R * NPR, keys) + 1))
+    g = torch.Generator().manual_seed(seed)
+    host_k = torch.randint(-30000, 30000, (keys * P, hkv * d), generator=g, dtype=torch.int16).pin_memory()
+    host_v = torch.randint(-30000, 30000, (keys * P, hkv * d), generator=g, dtype=torch.int16).pin_memory()
+    cache = tsa.KvPool(capacity, P, hkv, d, d)
+    tier = tsa.LruTier(cache, L, R, NPR, host_k, host_v)
+    ck = cache.k.view(torch.int16).view(capacity * P, hkv * d)
+    cv = cache.v.view(torch.int16).view(capacity * P, hkv * d)
+    print(f"[random tier {seed}] P {P} hkv {hkv} d {d} layers {L} requests {R} pages {NPR} "
+          f"capacity {capacity}", flush=True)
+    held, tag, checked = [], 0, 0
+    for step in range(3):
+        for layer in range(L):
+            k = int(rng.integers(1, min(NPR * P, 256) + 1))
+            pos = np.full((R, k), -1, dtype=np.int32)
+            for r in range(R):
+                m = int(rng.integers(0, k + 1))
+                pos[r, :m] = np.sort(rng.choice(NPR * P, size=m, replace=False))
+            try:
+                table, _ = tier.plan(layer, tag, pos)
+            except tsa.TsaError:
+                for t in held:
+                    tier.release(t)
+                held = []
+                tag += 1
+                continue
+            table_dev = torch.full((R, NPR), -1, dtype=torch.int32, device="cuda")
+            tier.fetch(table_dev)
+            torch.cuda.synchronize()
+            assert np.array_equal(table_dev.cpu().numpy(), table)
+            hk, hv = ck.cpu().numpy(), cv.cpu().numpy()
+            for r, page in zip(*np.nonzero(table >= 0)):
+                key = (layer * R + int(r)) * NPR + int(page)
+                s = int(table[r, page])
+                assert np.array_equal(hk[s * P:(s + 1) * P], host_k[key * P:(key + 1) * P].numpy()), (r, page)
+                assert np.array_equal(hv[s * P:(s + 1) * P], host_v[key * P:(key + 1) * P].numpy()), (r, page)
+                checked += 1
+            held.append(tag)
+            tag += 1
+            if rng.random() < 0.6:
+                chosen = [int(i) for i in rng.permutation(len(held))[:int(rng.integers(1, len(held) + 1))]]
+                for i in chosen:
+                    tier.release(held[i])
+                held = [t for j, t in enumerate(held) if j not in chosen]
+    assert checked > 0

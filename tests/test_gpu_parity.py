@@ -301,9 +301,10 @@ def test_topk_random_floats(tsa):
         assert np.array_equal(got[b], otopk.select_padded(s[b, :lens[b]], k)), f"row {b}"
 
 
-@pytest.mark.parametrize("max_len", [901, 2000, 4000, 8000, 12001, 16000, 24000, 32768, 48000, 65536])
+@pytest.mark.parametrize("max_len", [300, 901, 2000, 3000, 8000, 12001, 16000, 24000, 32768, 48000, 65536])
 def test_topk_every_launch_shape(tsa, max_len):
-    """One max length per scores-per-thread class of the top-k launch (1 .. 64 per thread):
+    """One max length per launch shape of the top-k (512 threads with 1, 2 or 4 scores each up to
+    2,048 scores, then 1,024 threads with 4 .. 64):
     rows of floats with repeated values, integer-valued rows with many ties, and a row of one
     repeated value; lengths drawn up to max_len (two odd maxima take the scalar score loads).
     Bit-exact against the oracle's selection."""
@@ -325,31 +326,42 @@ def test_topk_every_launch_shape(tsa, max_len):
         assert np.array_equal(got[b], otopk.select_padded(s[b, :lens[b]], k)), f"row {b}, len {lens[b]}"
 
 
-def test_topk_signed_zeros_and_nans(tsa):
+@pytest.mark.parametrize("L", [700, 6000, 20000])
+def test_topk_signed_zeros_and_nans(tsa, L):
     """Scores compared as floats, as the oracle does: -0 equals +0 (ties by position) and a NaN
-    ranks below every number (NaNs by position).  Row 0 keeps only numbers (the list path),
-    row 1 needs some of its NaNs (the general path), row 2 is zeros of both signs and a few
-    denormals of either sign (kept apart from the zeros: no flush to zero)."""
-    rng = np.random.default_rng(21)
-    L, k = 6000, 512
-    s = np.zeros((3, L), dtype=np.float32)
+    ranks below every number (NaNs by position).  Row 0 is mostly zeros of both signs with NaNs,
+    row 1 needs some of its NaNs, row 2 is zeros of both signs and a few denormals of either sign
+    (kept apart from the zeros: no flush to zero); these three take the register passes at every
+    length.  Row 3 has fewer positive scores than k, then zeros of both signs, NaNs and negative
+    scores: the k-th score is a zero, and at 20,000 scores the row takes the sampled list.  The
+    lengths cover the 512-thread launch (700) and two 1,024-thread ones."""
+    rng = np.random.default_rng(21 + L)
+    k = 64 if L < 2048 else 512
+    s = np.zeros((4, L), dtype=np.float32)
     s[0] = np.round(rng.normal(0, 0.2, size=L))            # mostly zeros: the k-th score is 0
-    s[0, rng.choice(L, 300, replace=False)] = np.nan
+    s[0, rng.choice(L, L // 20, replace=False)] = np.nan
     s[0, ::3] = -s[0, ::3]                                 # -0 among the zeros
     s[1] = np.nan
-    s[1, rng.choice(L, 400, replace=False)] = -0.0
-    s[1, rng.choice(L, 50, replace=False)] = 1.5
+    s[1, rng.choice(L, L // 15, replace=False)] = -0.0
+    s[1, rng.choice(L, k // 10, replace=False)] = 1.5
     s[2] = np.where(rng.random(L) < 0.5, -0.0, 0.0)
     s[2, rng.choice(L, 40, replace=False)] = np.float32(1e-40)    # denormals rank above the zeros
     s[2, rng.choice(L, 40, replace=False)] = np.float32(-1e-40)   # ... and below them
-    lens = np.array([L, L, L], dtype=np.int32)
-    p = tsa.decode_params(3, 8, k, L, 1.0)
-    out = torch.empty((3, k), dtype=torch.int32, device="cuda")
+    order = rng.permutation(L)
+    n_pos, n_zero, n_nan = 3 * k // 4, 4 * k, L // 100
+    s[3] = rng.normal(-3, 1, size=L)
+    s[3, order[:n_pos]] = rng.normal(5, 1, size=n_pos)
+    s[3, order[n_pos:n_pos + n_zero]] = np.where(rng.random(n_zero) < 0.5, -0.0, 0.0)
+    s[3, order[n_pos + n_zero:n_pos + n_zero + n_nan]] = np.nan
+    lens = np.full(4, L, dtype=np.int32)
+    p = tsa.decode_params(4, 8, k, L, 1.0)
+    out = torch.empty((4, k), dtype=torch.int32, device="cuda")
+    print(f"[topk] signed zeros, L {L}", flush=True)
     tsa.topk(p, torch.from_numpy(s).cuda(), torch.from_numpy(lens).cuda(), out)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
-    assert np.signbit(s[0][s[0] == 0]).any() and np.signbit(s[2]).any()
-    for b in range(3):
+    assert np.signbit(s[0][s[0] == 0]).any() and np.signbit(s[2]).any() and np.signbit(s[3][s[3] == 0]).any()
+    for b in range(4):
         assert np.array_equal(got[b], otopk.select_padded(s[b], k)), f"row {b}"
 
 

@@ -525,14 +525,22 @@ bool topk_supported(int max_len) { return max_len <= 64 * kMaxThreads; }
 
 hipError_t launch_topk(const tsa_decode_params& p, const float* scores, int ld,
                        const int32_t* seq_lens, int32_t* topk, hipStream_t s) {
-    // 1,024 threads always: the phases are latency-bound, and sixteen waves hide one another's
-    // latency better than fewer waves with more elements each (256 or 512 threads measured 10 to
-    // 70 % slower).  The scores per thread follow the length closely, since every pass walks all
-    // of them (24 instead of 32 per thread took a 20k-token selection from 13.2 to 12.6 us).
+    // 1,024 threads from 2,049 scores up: the phases are latency-bound, and sixteen waves hide one
+    // another's latency better than fewer waves with more elements each (256 or 512 threads
+    // measured 10 to 70 % slower there).  Up to 2,048 scores, 512 threads with 1, 2 or 4 scores
+    // each are 0.4-0.7 us faster than 1,024 with 1 or 2 (half the waves go through each barrier)
+    // and 256 threads are slower again.  The scores per thread follow the length closely, since
+    // every pass walks all of them (24 instead of 32 per thread took a 20k-token selection from
+    // 13.2 to 12.6 us).
+    if (p.max_len <= 2048) {
+        const int ipt = (p.max_len + 511) / 512;
+        if (ipt <= 1) launch_shape<1, 512>(p, scores, ld, seq_lens, topk, s);
+        else if (ipt <= 2) launch_shape<2, 512>(p, scores, ld, seq_lens, topk, s);
+        else launch_shape<4, 512>(p, scores, ld, seq_lens, topk, s);
+        return hipGetLastError();
+    }
     const int ipt = (p.max_len + kMaxThreads - 1) / kMaxThreads;
-    if (ipt <= 1) launch_shape<1, 1024>(p, scores, ld, seq_lens, topk, s);
-    else if (ipt <= 2) launch_shape<2, 1024>(p, scores, ld, seq_lens, topk, s);
-    else if (ipt <= 4) launch_shape<4, 1024>(p, scores, ld, seq_lens, topk, s);
+    if (ipt <= 4) launch_shape<4, 1024>(p, scores, ld, seq_lens, topk, s);
     else if (ipt <= 8) launch_shape<8, 1024>(p, scores, ld, seq_lens, topk, s);
     else if (ipt <= 12) launch_shape<12, 1024>(p, scores, ld, seq_lens, topk, s);
     else if (ipt <= 16) launch_shape<16, 1024>(p, scores, ld, seq_lens, topk, s);

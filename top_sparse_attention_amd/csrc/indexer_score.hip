@@ -117,12 +117,8 @@ __global__ void __launch_bounds__(kThreads) indexer_score_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Single-head indexer (the common case): every wave streams its own run of tokens through a
-// private ring of LDS slots with global-to-LDS loads, which sustain more HBM bandwidth than
-// loads into registers.  A slot holds 16 token rows; lane (j16, g16) dots row j16's quarter
-// g16 with the matching quarter of the query, and the four quarters are summed with the
-// cross-half lane swaps.  Rows are stored with their 16-byte chunks XOR-swizzled so that the
-// 16 rows read in parallel fall on distinct LDS banks.
+// Runs of tokens per wave, the LDS ring of the multi-head kernel and the score stage of both
+// streaming kernels.
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr int kRing = 4;              // slots per wave
@@ -173,6 +169,7 @@ __device__ __forceinline__ int idx_swz(int r, int c) {
 }
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
@@ -260,15 +257,146 @@ __global__ void __launch_bounds__(256) append_last_kernel(AppendLast f, int batc
                 page_size, num_pages, seq_lens, max_len, false, nullptr, nullptr, 0, 0, nullptr, 0);
 }
 
+// Single-head indexer, register stream.  Wave w owns a run of one request's tokens.  One
+// wave-wide load brings 1 KiB = kRowsPerLoad key rows into registers (each row spread over
+// D/8 lanes, 16 bytes each, with the non-temporal policy); each lane dots its 8 dims with the
+// matching 8 query dims (four v_dot2 on bf16 pairs), and a DPP sum over the row's lanes gives
+// the token's dot product.  A batch of kStreamLoads loads is issued before any is used.  Scores
+// are staged in LDS and stored kStage at a time with 16-byte stores.  On 64 x 32k tokens this
+// streams 545 MB in 82 us against 87 us for the LDS-ring kernel below, which the multi-head
+// indexer keeps for its matrix-core layout.
+template <int D>
+struct StreamGeo {
+    static constexpr int kLanesPerRow = D / 8;
+    static constexpr int kRowsPerLoad = 64 / kLanesPerRow;
+    static_assert(kLanesPerRow >= 4 && kLanesPerRow <= 32, "D in 32 .. 256");
+};
+constexpr int kStreamLoads = 4;      // wave loads per batch (4 measured faster than 2, 8 or 16, and
+                                      // than keeping two batches in flight)
+constexpr int kStreamWaves = 4096;    // waves per launch over the whole batch
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// sum over each aligned group of L lanes (L = 4, 8, 16 or 32), the result in every lane
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+    x = dpp_add<0xB1>(x);                         // quad_perm [1, 0, 3, 2]
+    x = dpp_add<0x4E>(x);                         // quad_perm [2, 3, 0, 1]
+    if constexpr (L >= 8) x = dpp_add<0x141>(x);  // row_half_mirror: the other quad of 8
+    if constexpr (L >= 16) x = dpp_add<0x140>(x); // row_mirror: the other half of 16
+    if constexpr (L >= 32) {
+        const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    }
+    return x;
+}
+
+template <int D, bool ALIGNED>
+__global__ void __launch_bounds__(256) indexer_score_stream_kernel(
+    const uint16_t* __restrict__ qidx, const float* __restrict__ widx,
+    const int32_t* __restrict__ page_table, int max_pages, int page_size, int page_shift,
+    int num_pages, const int32_t* __restrict__ seq_lens, int max_len,
+    const uint16_t* __restrict__ kpool, float* __restrict__ scores, int ld, int tok_per_wave,
+    int batch, AppendLast fused) {
+    using G = StreamGeo<D>;
+    constexpr int R = G::kRowsPerLoad, U = kStreamLoads;
+    static_assert(kStage % (U * R) == 0, "a stage is a whole number of batches");
+    __shared__ int32_t wpages[4][kPagesPerWave];   // page ids of each wave's token run
+    __shared__ __align__(16) float stage[4][kStage];
+    const bool append = fused.k_src != nullptr;
+    if (append && blockIdx.y == 0) {     // the first row of workgroups (dispatched first): the new tokens
+        append_last(fused, blockIdx.x * 4 + (threadIdx.x >> 6), gridDim.x * 4, batch, page_table,
+                    max_pages, page_size, num_pages, seq_lens, max_len, true, qidx, widx, 1, D, scores, ld);
+        return;
+    }
+    const int b = blockIdx.y - (append ? 1 : 0);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane / G::kLanesPerRow, c = lane % G::kLanesPerRow;
+    int len = seq_lens[b];
+    len = len < 0 ? 0 : (len > max_len ? max_len : len);
+    const int t0 = (blockIdx.x * 4 + wave) * tok_per_wave;
+    const int t1 = min(t0 + tok_per_wave, append ? len - 1 : len);   // the new token is scored above
+    if (t0 >= t1) return;
+    const int32_t* pt = page_table + int64_t(b) * max_pages;
+    const int pg0 = ALIGNED ? (t0 >> page_shift) : t0 / page_size;
+    const int pg1 = ALIGNED ? ((t1 - 1) >> page_shift) : (t1 - 1) / page_size;
+    int32_t* wp = wpages[wave];
+    for (int i = lane; i <= pg1 - pg0; i += 64) {
+        const int32_t pid = pt[pg0 + i];
+        wp[i] = (pid >= 0 && pid < num_pages) ? pid : -1;
+    }
+    uint32_t q[4];
+    {
+        const uint4 v = reinterpret_cast<const uint4*>(qidx + int64_t(b) * D)[c];
+        q[0] = v.x; q[1] = v.y; q[2] = v.z; q[3] = v.w;
+    }
+    const float w = widx[0];
+    float* srow = scores + int64_t(b) * ld;
+    float* st = stage[wave];
+    const int n_loads = (t1 - t0 + R - 1) / R;
+    auto issue = [&](uint4 (&v)[U], int (&pgs)[U], int i) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            // the row this lane loads: token t (clamped into the run, masked below)
+            const int t = min(t0 + (i + u) * R + r, t1 - 1);
+            pgs[u] = ALIGNED ? wp[(t >> page_shift) - pg0] : wp[t / page_size - pg0];
+            const int off = ALIGNED ? (t & (page_size - 1)) : t % page_size;
+            const int64_t row = pgs[u] >= 0 ? int64_t(pgs[u]) * page_size + off : 0;
+            const uint4* src = reinterpret_cast<const uint4*>(kpool + row * D) + c;
+            v[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src)));
+        }
+    };
+    auto consume = [&](const uint4 (&v)[U], const int (&pgs)[U], int i) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float d = dot2(q[0], v[u].x, 0.f);
+            d = dot2(q[1], v[u].y, d);
+            d = dot2(q[2], v[u].z, d);
+            d = dot2(q[3], v[u].w, d);
+            d = group_sum<G::kLanesPerRow>(d);
+            const int rel = (i + u) * R + r;
+            if (c == 0 && t0 + rel < t1) st[rel & (kStage - 1)] = pgs[u] >= 0 ? w * fmaxf(d, 0.f) : -INFINITY;
+        }
+        // Scores leave in bursts of kStage (16-byte stores of a contiguous run) rather than a few
+        // bytes per load: stores spread between the key loads cost the stream several percent.
+        if (((i + U) * R) % kStage == 0 || i + U >= n_loads) {
+            const int s0 = ((i * R) / kStage) * kStage;        // run-relative start of this stage
+            const int n = min(kStage, t1 - t0 - s0);
+            float* dst = srow + t0 + s0;
+            if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {     // the workspace's rows always are
+                for (int e = 4 * lane; e < n; e += 256) {
+                    if (e + 4 <= n)
+                        *reinterpret_cast<float4*>(dst + e) = *reinterpret_cast<const float4*>(st + e);
+                    else
+                        for (int f = e; f < n; ++f) dst[f] = st[f];
+                }
+            } else {
+                for (int e = lane; e < n; e += 64) dst[e] = st[e];
+            }
+        }
+    };
+    for (int i = 0; i < n_loads; i += U) {
+        uint4 v[U];
+        int pgs[U];
+        issue(v, pgs, i);
+        consume(v, pgs, i);
+    }
+}
+
+// Multi-head indexer (LDS ring).  Every wave streams its own run of tokens through a private
+// ring of LDS slots with global-to-LDS loads.  A slot holds 16 token rows, stored with their
+// 16-byte chunks XOR-swizzled so that the 16 rows read in parallel fall on distinct LDS banks.
 // ALIGNED: page_size is a power of two and a multiple of the 16-token slot, so every slot lies in
 // one page and the page id is the same for the whole wave.
 //
-// NB = 0: one head, dotted on the vector ALUs (v_dot2 on bf16 pairs).
-// NB > 0: H <= 16 NB heads on the matrix cores.  The heads are the rows and the slot's 16 tokens
+// H <= 16 NB heads on the matrix cores.  The heads are the rows and the slot's 16 tokens
 // the columns of S = Q K^T, one 16 x 16 x 32 MFMA per (16-head block, 32 dims).  The contraction
 // index is free to be relabelled, so MFMA k = 8 g + i of step c stands for dim g * D/4 + 8 c + i:
-// lane group g (lanes 16 g .. 16 g + 15) then reads the same quarter of its token's row as in the
-// one-head case, and the query registers follow the same relabelling.  The MFMA leaves heads
+// lane group g (lanes 16 g .. 16 g + 15) then reads one quarter of its token's row, and the query
+// registers follow the same relabelling.  The MFMA leaves heads
 // 4 g .. 4 g + 3 of every block with lane group g, so each lane applies ReLU and the weights to
 // its heads and the four groups are summed across lanes.  Heads H .. 16 NB - 1 are zero rows
 // with weight 0 and add exactly 0.
@@ -280,14 +408,15 @@ __global__ void __launch_bounds__(256) indexer_score_lds_kernel(
     const uint16_t* __restrict__ kpool, float* __restrict__ scores, int ld, int tok_per_wave,
     int batch, AppendLast fused) {
     using G = IdxGeo<D>;
+    static_assert(NB > 0, "one head takes the register stream kernel");
     __shared__ __align__(16) unsigned char ring[4][kRing][G::kSlotBytes];
     __shared__ int32_t wpages[4][kPagesPerWave];   // page ids of each wave's token run
     __shared__ __align__(16) float stage[4][kStage];   // scores of each wave, stored kStage at a time
     const bool append = fused.k_src != nullptr;
     if (append && blockIdx.y == 0) {     // the first row of workgroups (dispatched first): the new tokens
         append_last(fused, blockIdx.x * 4 + (threadIdx.x >> 6), gridDim.x * 4, batch, page_table,
-                    max_pages, page_size, num_pages, seq_lens, max_len, true, qidx, widx,
-                    NB == 0 ? 1 : H, D, scores, ld);
+                    max_pages, page_size, num_pages, seq_lens, max_len, true, qidx, widx, H, D,
+                    scores, ld);
         return;
     }
     const int b = blockIdx.y - (append ? 1 : 0);
@@ -309,22 +438,11 @@ __global__ void __launch_bounds__(256) indexer_score_lds_kernel(
         wp[i] = (pid >= 0 && pid < num_pages) ? pid : -1;
     }
 
-    // NB = 0: query quarter g16 of this lane, as bf16 pairs
-    uint32_t q[NB == 0 ? G::kPart / 2 : 1];
-    float w = 0.f;
-    // NB > 0: rows of head j16 of every block (the MFMA A operand), and the weights of the
-    // heads this lane's accumulator rows hold
-    uint4 qm[NB > 0 ? NB : 1][G::kPartChunks];
-    float wm[NB > 0 ? NB : 1][4];
-    if constexpr (NB == 0) {
-        const uint4* src = reinterpret_cast<const uint4*>(qidx + int64_t(b) * D + g16 * G::kPart);
-#pragma unroll
-        for (int c = 0; c < G::kPartChunks; ++c) {
-            const uint4 v = src[c];
-            q[4 * c + 0] = v.x; q[4 * c + 1] = v.y; q[4 * c + 2] = v.z; q[4 * c + 3] = v.w;
-        }
-        w = widx[0];
-    } else {
+    // rows of head j16 of every block (the MFMA A operand), and the weights of the heads this
+    // lane's accumulator rows hold
+    uint4 qm[NB][G::kPartChunks];
+    float wm[NB][4];
+    {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int h = nb * 16 + j16;
@@ -397,19 +515,7 @@ __global__ void __launch_bounds__(256) indexer_score_lds_kernel(
         }
         const unsigned char* slot = &ring[wave][u % kRing][0];
         float sc;
-        if constexpr (NB == 0) {
-            float d = 0.f;
-#pragma unroll
-            for (int c = 0; c < G::kPartChunks; ++c) {
-                const uint4 v = *reinterpret_cast<const uint4*>(slot + rd_off[c]);
-                d = dot2(q[4 * c + 0], v.x, d);
-                d = dot2(q[4 * c + 1], v.y, d);
-                d = dot2(q[4 * c + 2], v.z, d);
-                d = dot2(q[4 * c + 3], v.w, d);
-            }
-            d = sum4groups(d);
-            sc = w * fmaxf(d, 0.f);
-        } else {
+        {
             f32x4 acc[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -487,12 +593,39 @@ hipError_t launch_lds(const tsa_kv_pool& pool, int layer, const tsa_decode_param
 }
 
 template <int D>
+hipError_t launch_stream(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
+                         const void* qidx, const float* widx, const int32_t* page_table,
+                         int max_pages, const int32_t* seq_lens, float* scores, int ld,
+                         hipStream_t s, int shift, const AppendLast& fused) {
+    const tsa_pool_desc& d = pool.d;
+    // about 4096 waves over the whole batch (16 per CU), at least a few loads each
+    const int64_t total = int64_t(p.batch) * p.max_len;
+    int tpw = int((total + kStreamWaves - 1) / kStreamWaves);
+    tpw = std::max(kUnit * 4, std::min(tpw, kMaxTpw));
+    tpw = (tpw + kUnit - 1) / kUnit * kUnit;
+    dim3 grid(std::max(1, (p.max_len + 4 * tpw - 1) / (4 * tpw)), p.batch + (fused.k_src ? 1 : 0));
+    const uint16_t* kpool = static_cast<const uint16_t*>(pool.idx) + int64_t(layer) * pool.slots() * D;
+    const bool aligned = shift >= 0 && d.page_size % kUnit == 0;
+    if (aligned)
+        hipLaunchKernelGGL((indexer_score_stream_kernel<D, true>), grid, dim3(256), 0, s,
+                           static_cast<const uint16_t*>(qidx), widx, page_table, max_pages,
+                           d.page_size, shift, d.num_pages, seq_lens, p.max_len, kpool, scores, ld, tpw,
+                           p.batch, fused);
+    else
+        hipLaunchKernelGGL((indexer_score_stream_kernel<D, false>), grid, dim3(256), 0, s,
+                           static_cast<const uint16_t*>(qidx), widx, page_table, max_pages,
+                           d.page_size, shift, d.num_pages, seq_lens, p.max_len, kpool, scores, ld, tpw,
+                           p.batch, fused);
+    return hipGetLastError();
+}
+
+template <int D>
 hipError_t launch_lds_heads(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                             const void* qidx, const float* widx, const int32_t* page_table,
                             int max_pages, const int32_t* seq_lens, float* scores, int ld,
                             hipStream_t s, int shift, const AppendLast& f) {
     const int h = p.index_heads;
-    if (h == 1) return launch_lds<D, 0>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift, f);
+    if (h == 1) return launch_stream<D>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift, f);
     if (h <= 16) return launch_lds<D, 1>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift, f);
     if (h <= 32) return launch_lds<D, 2>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift, f);
     if (h <= tsa::kMaxIndexHeads) return launch_lds<D, 4>(pool, layer, p, qidx, widx, page_table, max_pages, seq_lens, scores, ld, s, shift, f);

@@ -263,8 +263,10 @@ __global__ void __launch_bounds__(256) append_last_kernel(AppendLast f, int batc
 // matching 8 query dims (four v_dot2 on bf16 pairs), and a DPP sum over the row's lanes gives
 // the token's dot product.  A batch of kStreamLoads loads is issued before any is used.  Scores
 // are staged in LDS and stored kStage at a time with 16-byte stores.  On 64 x 32k tokens this
-// streams 545 MB in 82 us against 87 us for the LDS-ring kernel below, which the multi-head
-// indexer keeps for its matrix-core layout.
+// streams 545 MB in 82 us against 87 us for the LDS-ring kernel below.  The multi-head indexer
+// keeps the LDS ring: its matrix-core version of this stream (query rows of 64 heads held in
+// registers, 16-token slots loaded in the MFMA operand order) measured 107-132 us against 94 us,
+// since the registers the queries take leave too few waves and loads in flight.
 template <int D>
 struct StreamGeo {
     static constexpr int kLanesPerRow = D / 8;

@@ -23,6 +23,11 @@
 //                      shuffle.
 // Rows are stored with their 16-byte chunks XOR-swizzled by row, so the rows an MFMA operand read
 // touches fall on distinct LDS banks (on 16 bank groups; 64-dim rows, 8 chunks wide, pair up).
+//
+// With few (request, KV head) pairs (at most 256: one workgroup per CU), the splits of a pair run
+// as the waves of one workgroup instead (kMergeWaves of them), each exactly as above, and merge
+// their running max, sum and accumulator through LDS at the end: the split partials never reach
+// memory and the step needs no combine launch.
 #include "tsa_internal.h"
 #include "mfma_lds.h"
 
@@ -38,6 +43,7 @@ constexpr int kTileG = 32;                       // rows per tile
 constexpr int kRingG = 2;                        // tiles per wave in LDS (the loop assumes 2)
 constexpr int kUnitsPerWg = 1;                   // waves (units) per workgroup
 constexpr int kRowsMaxG = 1024;                  // selected rows per unit (its LDS row list)
+constexpr int kMergeWaves = 4;                   // splits merged inside one workgroup
 constexpr float kLog2eG = 1.4426950408889634f;
 
 template <int DK, int DV>
@@ -77,15 +83,17 @@ struct GqaArgs {
     float scale_log2;           // sm_scale * log2(e)
 };
 
-template <int DK, int DV>
-__global__ void __launch_bounds__(64 * kUnitsPerWg) attn_gqa_kernel(GqaArgs a) {
+// W = 1: one independent unit per workgroup; W = kMergeWaves: workgroup = (request, KV head), wave
+// = split, merged in LDS at the end.
+template <int DK, int DV, int W>
+__global__ void __launch_bounds__(64 * W) attn_gqa_kernel(GqaArgs a) {
     using Geo = GqaGeo<DK, DV>;
     constexpr int CK = Geo::kChunksK, CV = Geo::kChunksV;
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int unit = blockIdx.x * kUnitsPerWg + wave;
-    if (unit >= a.n_units) return;                      // uniform: the whole wave
+    const int unit = W == 1 ? int(blockIdx.x) * kUnitsPerWg + wave : int(blockIdx.x) * W + wave;
+    if (unit >= a.n_units) return;                      // uniform (W > 1: every wave of the group)
     unsigned char* ring = smem + wave * Geo::kWaveLds;
     int32_t* rows = reinterpret_cast<int32_t*>(ring + kRingG * Geo::kTileBytes);
     const int s_idx = unit % a.splits;
@@ -242,6 +250,42 @@ __global__ void __launch_bounds__(64 * kUnitsPerWg) attn_gqa_kernel(GqaArgs a) {
     }
 
     const float l_tot = sum4groups(l_run);
+    if constexpr (W > 1) {
+        // each wave leaves (max, sum) of its lanes' heads and its O^T blocks in its own ring, which
+        // only it has used; after the barrier wave w writes output blocks w, w + W, ...
+        float* mine = reinterpret_cast<float*>(ring);
+        f32x4* macc = reinterpret_cast<f32x4*>(ring + 512);
+        mine[lane] = m_run;
+        mine[64 + lane] = l_tot;
+#pragma unroll
+        for (int db = 0; db < DV / 16; ++db) macc[db * 64 + lane] = acc[db];
+        __syncthreads();
+        float wt[W];
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            wt[w] = reinterpret_cast<const float*>(smem + w * Geo::kWaveLds)[lane];
+            M = fmaxf(M, wt[w]);
+        }
+        float L = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            // a split without tokens has max -inf, sum 0 and a zero accumulator
+            wt[w] = wt[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(wt[w] - M);
+            L += wt[w] * reinterpret_cast<const float*>(smem + w * Geo::kWaveLds)[64 + lane];
+        }
+        if (j16 >= G) return;
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        float* o = a.out + (int64_t(b) * a.hq + h0 + j16) * DV;
+        for (int db = wave; db < DV / 16; db += W) {
+            f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < W; ++w)
+                x += wt[w] * reinterpret_cast<const f32x4*>(smem + w * Geo::kWaveLds + 512)[db * 64 + lane];
+            *reinterpret_cast<float4*>(o + db * 16 + 4 * g16) = make_float4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+        }
+        return;
+    }
     if (j16 >= G) return;
     const int h = h0 + j16;
     if (a.splits == 1) {
@@ -279,16 +323,27 @@ size_t gqa_wave_lds(int dk, int dv) {
     return 0;
 }
 
-template <int DK, int DV>
-hipError_t launch_gqa(const GqaArgs& a, hipStream_t s) {
-    auto kern = attn_gqa_kernel<DK, DV>;
-    const size_t smem = size_t(kUnitsPerWg) * GqaGeo<DK, DV>::kWaveLds;
+template <int DK, int DV, int W>
+hipError_t launch_gqa_w(const GqaArgs& a, hipStream_t s) {
+    auto kern = attn_gqa_kernel<DK, DV, W>;
+    const int per_wg = W == 1 ? kUnitsPerWg : W;
+    const size_t smem = size_t(per_wg) * GqaGeo<DK, DV>::kWaveLds;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
     if (e != hipSuccess) return e;
-    const int wgs = (a.n_units + kUnitsPerWg - 1) / kUnitsPerWg;
-    hipLaunchKernelGGL(kern, dim3(wgs), dim3(64 * kUnitsPerWg), smem, s, a);
+    const int wgs = (a.n_units + per_wg - 1) / per_wg;
+    hipLaunchKernelGGL(kern, dim3(wgs), dim3(64 * per_wg), smem, s, a);
     return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_gqa(const GqaArgs& a, bool merge, hipStream_t s) {
+    if constexpr (kMergeWaves * GqaGeo<DK, DV>::kWaveLds <= 160 * 1024) {
+        if (merge) return launch_gqa_w<DK, DV, kMergeWaves>(a, s);
+    } else {
+        if (merge) return hipErrorInvalidValue;
+    }
+    return launch_gqa_w<DK, DV, 1>(a, s);
 }
 
 }  // namespace
@@ -335,6 +390,17 @@ int gqa_mfma_chunk(const tsa_kv_pool& pool, const tsa_decode_params& p, int* spl
     return chunk;
 }
 
+// Splits merged inside the workgroup: for 64 to 256 (request, KV head) pairs (one workgroup of
+// kMergeWaves waves per CU at most, and at least a quarter of the CUs busy), selections of at
+// least one tile per wave, and head dims whose kMergeWaves rings fit in LDS.
+bool gqa_wg_merge(const tsa_kv_pool& pool, const tsa_decode_params& p) {
+    const int64_t base = int64_t(p.batch) * pool.d.num_kv_heads;
+    const int k_eff = std::max(1, std::min(p.top_k, p.max_len));
+    const size_t lds = gqa_wave_lds(pool.d.head_dim_k, pool.d.head_dim_v);
+    return base >= 64 && base <= 256 && k_eff >= kMergeWaves * kTileG && lds > 0 &&
+           kMergeWaves * lds <= 160 * 1024 && ceil_div(k_eff, kMergeWaves) <= kRowsMaxG;
+}
+
 hipError_t launch_attention_gqa(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                                 const AttnPlan& plan, const void* q, const int32_t* topk,
                                 const int32_t* page_table, int max_pages, const int32_t* seq_lens,
@@ -362,10 +428,11 @@ hipError_t launch_attention_gqa(const tsa_kv_pool& pool, int layer, const tsa_de
     a.chunk = plan.chunk;
     a.n_units = p.batch * d.num_kv_heads * plan.splits;
     a.scale_log2 = p.sm_scale * kLog2eG;
-    if (d.head_dim_k == 64) return launch_gqa<64, 64>(a, s);
-    if (d.head_dim_k == 128) return launch_gqa<128, 128>(a, s);
-    if (d.head_dim_k == 192) return launch_gqa<192, 128>(a, s);
-    if (d.head_dim_k == 256) return launch_gqa<256, 256>(a, s);
+    if (plan.wg_merge && plan.splits != kMergeWaves) return hipErrorInvalidValue;
+    if (d.head_dim_k == 64) return launch_gqa<64, 64>(a, plan.wg_merge, s);
+    if (d.head_dim_k == 128) return launch_gqa<128, 128>(a, plan.wg_merge, s);
+    if (d.head_dim_k == 192) return launch_gqa<192, 128>(a, plan.wg_merge, s);
+    if (d.head_dim_k == 256) return launch_gqa<256, 256>(a, plan.wg_merge, s);
     return hipErrorInvalidValue;
 }
 

@@ -402,6 +402,14 @@ AttnPlan plan_attention(const tsa_kv_pool& pool, const tsa_decode_params& p) {
     }
     if (gqa_mfma_applicable(pool, p)) {
         plan.kind = 2;
+        if (gqa_wg_merge(pool, p)) {
+            const int k_eff = std::max(1, std::min(p.top_k, p.max_len));
+            plan.wg_merge = true;
+            plan.splits = kGqaMergeSplits;
+            plan.chunk = int(ceil_div(ceil_div(k_eff, kGqaMergeSplits), 32)) * 32;
+            plan.partial_bytes = 0;
+            return plan;
+        }
         plan.chunk = gqa_mfma_chunk(pool, p, &plan.splits);
         plan.partial_bytes = plan.splits > 1 ? partial_bytes(size_t(p.batch) * p.num_q_heads * plan.splits,
                                                              d.head_dim_v)
@@ -473,7 +481,7 @@ hipError_t launch_attention(const tsa_kv_pool& pool, int layer, const tsa_decode
     } else {
         e = launch_valu(a, pool, p, plan, s);
     }
-    if (e != hipSuccess || plan.splits == 1) return e;
+    if (e != hipSuccess || plan.splits == 1 || plan.wg_merge) return e;
     if (plan.splits <= kSmallSplits)
         hipLaunchKernelGGL(combine_small_kernel, dim3(p.batch * p.num_q_heads), dim3(kCombineThreads), 0, s,
                            a.part_ml, a.part_acc, plan.splits, d.head_dim_v, out);

@@ -86,6 +86,7 @@ struct AttnPlan {
     int splits = 1;       // workgroups per (request, KV head) along the selected tokens
     int chunk = 0;        // selected tokens per split
     size_t partial_bytes = 0;
+    bool wg_merge = false;   // grouped-query kernel: the splits of a pair merge inside one workgroup
 };
 AttnPlan plan_attention(const tsa_kv_pool& pool, const tsa_decode_params& p);
 bool attention_supported(const tsa_kv_pool& pool, const tsa_decode_params& p, std::string* why);
@@ -99,6 +100,8 @@ hipError_t launch_attention_mfma(const tsa_kv_pool& pool, int layer, const tsa_d
 // Matrix-core kernel for grouped-query shapes (128-dim keys and values, up to 16 q heads per KV head).
 bool gqa_mfma_applicable(const tsa_kv_pool& pool, const tsa_decode_params& p);
 int gqa_mfma_chunk(const tsa_kv_pool& pool, const tsa_decode_params& p, int* splits);
+bool gqa_wg_merge(const tsa_kv_pool& pool, const tsa_decode_params& p);
+constexpr int kGqaMergeSplits = 4;
 hipError_t launch_attention_gqa(const tsa_kv_pool& pool, int layer, const tsa_decode_params& p,
                                 const AttnPlan& plan, const void* q, const int32_t* topk,
                                 const int32_t* page_table, int max_pages, const int32_t* seq_lens,

@@ -54,7 +54,8 @@ def _scramble_last(st):
 @pytest.mark.parametrize("name,kw", [("tiny_b5", {}), ("gqa_b32_8k", {"batch": 6}),
                                      ("mla_b64_32k", {"batch": 3}),
                                      ("gqa_b32_8k", {"batch": 4, "index_heads": 16}),
-                                     ("gqa_b32_8k", {"lens": np.array([1, 9, 300, 2000], np.int32), "page_size": 8})])
+                                     ("gqa_b32_8k", {"lens": np.array([1, 9, 300, 2000], np.int32), "page_size": 8}),
+                                     ("prefix_b128_16k", {"batch": 6})])
 def test_decode_step_equals_separate_calls(tsa, name, kw):
     st = _stage(name, **kw)
     kn, vn, inew = _new_rows(st)

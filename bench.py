@@ -163,8 +163,8 @@ def _attn_src(w) -> str:
     if w.v_from_k:
         return "attn_mfma.hip"
     G = w.num_q_heads // w.num_kv_heads
-    if w.head_dim_k == 128 and w.head_dim_v == 128 and G <= 16:
-        return "attn_gqa.hip"
+    if (w.head_dim_k, w.head_dim_v) in ((64, 64), (128, 128), (192, 128), (256, 256)) and G <= 16:
+        return "attn_gqa.hip"      # the grouped-query matrix-core kernel's shapes
     return "attn_valu.hip"
 
 

@@ -612,7 +612,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the decode step is sharded by request with no exchange "
-              f"between GPUs, and this build runs no multi-GPU path (asked for --gpus {args.gpus}).",
+              f"between GPUs, and the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -42,7 +42,7 @@ typedef enum tsa_status {
     TSA_ERR_SHARED_PAGE_WRITE = -3, /* an append would write a page other tables also map */
     TSA_ERR_HIP = -4,               /* a HIP runtime call or kernel launch failed */
     TSA_ERR_CAPACITY = -5,          /* a caller-sized buffer (workspace, cache) is too small */
-    TSA_ERR_UNSUPPORTED = -6        /* a valid shape no kernel of this build handles */
+    TSA_ERR_UNSUPPORTED = -6        /* a valid shape no kernel of the library handles */
 } tsa_status;
 
 /* Message for the last failure on this thread ("" if none).  Valid until the next call. */

@@ -4,7 +4,7 @@ sequence through the library's tier (bookkeeping only, no GPU).
 GLM5.3 sparse-attention page, HiSparse paragraph: the HBM part of the KV cache is an LRU cache,
 a selection that misses loads the page from host memory and evicts the least recently used one,
 and layer N's loads overlap layer N-1's compute (so two layers' pages are in flight).  The plan
-policy is this build's reading (the page fixes no order): requests ascending, each request's
+policy is the library's reading (the page fixes no order): requests ascending, each request's
 distinct pages ascending, key = (layer * num_req + req) * pages_per_req + page, free slots taken
 lowest first, pages of unreleased plans pinned.
 

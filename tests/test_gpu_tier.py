@@ -190,6 +190,31 @@ def test_tier_outputs_match_oracle(tier_run):
     print(f"tier: max normwise error {worst:.2e}")
 
 
+@pytest.fixture(scope="module", params=["page", "token"])
+def tier_merge_run(tsa, request):
+    """32 requests x 2 KV heads: 64 (request, KV head) pairs, so the attention through the cache
+    runs the grouped-query kernel with the four splits of each pair merged in one workgroup."""
+    from top_sparse_attention_amd import workload
+    w = synth.get("tiered_b256_64k")
+    # whole pages: a layer's plan pins nearly every page of these short contexts, so the cache
+    # holds all of them; token rows: the default quarter, with evictions
+    cache_pages = 2 * 32 * (2048 // w.page_size) if request.param == "page" else None
+    st = workload.stage_tier(w, seed=1, num_req=32, length=2048, num_layers=2, top_k=256,
+                             cache_pages=cache_pages, unit=request.param)
+    outs, tables, positions = _run_tier(tsa, st, steps=2)
+    return st, outs, tables, positions
+
+
+def test_tier_with_merged_splits(tsa, tier_merge_run):
+    """Bookkeeping equal to the oracle's LRU, outputs through the cache bit-identical to a pool
+    holding every page, and sampled outputs within the bar of the fp64 oracle."""
+    st, outs, tables, positions = tier_merge_run
+    _bookkeeping(st, tables, positions)
+    _tier_off(tsa, st, outs, positions)
+    worst = _oracle_sampled(st, outs, positions, [(0, 0), (1, 31), (2, 17), (3, 5)])
+    print(f"tier, 32 requests: max normwise error {worst:.2e}")
+
+
 def test_tier_prefetch_equals_plan_and_fetch(tsa, tier_run):
     """tsa_lru_prefetch (plan + ordered fetch + fetched event in one call) gives the same outputs
     and counters as separate plan and fetch calls on a fresh tier over the same host copy."""

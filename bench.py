@@ -630,6 +630,30 @@ def main():
     bench_step(args)
 
 
+def _row_bytes(w) -> int:
+    """Bytes of one selected token's K (and V, when stored apart) over all KV heads, bf16."""
+    return w.num_kv_heads * w.head_dim_k * 2 + (0 if w.v_from_k else w.num_kv_heads * w.head_dim_v * 2)
+
+
+def algorithmic_counts(w, lens):
+    """Algorithmic bytes and FLOPs of one launch of the indexer score and of the gather-attention
+    (with its combine) over requests of lengths `lens`:
+      indexer:   every cached token's indexer key (bf16, D_I dims) read and its fp32 score written,
+                 2 * H_I * D_I FLOPs per token;
+      attention: min(len, k) selected rows per request (_row_bytes), the bf16 queries, the fp32
+                 outputs and the int32 top-k indices, 2 * Hq * (dk + dv) FLOPs per selected row.
+    Returns (indexer bytes, indexer FLOPs, attention bytes, attention FLOPs)."""
+    lens = np.asarray(lens, dtype=np.int64)
+    B, D_I = len(lens), w.index_dim
+    idx_bytes = int((lens * (2 * D_I + 4)).sum())
+    idx_flops = float(2 * w.index_heads * D_I * lens.sum())
+    n_sel = np.minimum(lens, w.top_k)
+    attn_bytes = int(n_sel.sum() * _row_bytes(w) + B * w.num_q_heads * w.head_dim_k * 2 +
+                     B * w.num_q_heads * w.head_dim_v * 4 + B * w.top_k * 4)
+    attn_flops = float(2 * n_sel.sum() * w.num_q_heads * (w.head_dim_k + w.head_dim_v))
+    return idx_bytes, idx_flops, attn_bytes, attn_flops
+
+
 def _pct(xs):
     xs = np.asarray(xs, dtype=np.float64)
     return {"median": round(float(np.median(xs)), 5), "p10": round(float(np.percentile(xs, 10)), 5),
@@ -757,13 +781,9 @@ def bench_step(args):
     # algorithmic bytes per launch
     lens = st.lens.astype(np.int64)
     D_I = w.index_dim
-    idx_bytes = int((lens * (2 * D_I + 4)).sum())
-    idx_flops = float(2 * w.index_heads * D_I * lens.sum())
+    idx_bytes, idx_flops, attn_bytes, attn_flops = algorithmic_counts(w, lens)
     n_sel = np.minimum(lens, w.top_k)
-    row = w.num_kv_heads * w.head_dim_k * 2 + (0 if w.v_from_k else w.num_kv_heads * w.head_dim_v * 2)
-    attn_bytes = int(n_sel.sum() * row + B * w.num_q_heads * w.head_dim_k * 2 +
-                     B * w.num_q_heads * w.head_dim_v * 4 + B * w.top_k * 4)
-    attn_flops = float(2 * n_sel.sum() * w.num_q_heads * (w.head_dim_k + w.head_dim_v))
+    row = _row_bytes(w)
 
     attn_src = _attn_src(w)
     # Bytes HBM must deliver at the least.  Requests of a shared-prefix workload alias the same

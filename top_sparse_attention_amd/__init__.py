@@ -28,7 +28,8 @@ __all__ = ["KvPool", "DecodeParams", "TsaError", "load", "decode_params", "works
 def _i32p(a: Optional[np.ndarray]):
     if a is None:
         return None
-    assert a.dtype == np.int32 and a.flags.c_contiguous
+    if a.dtype != np.int32 or not a.flags.c_contiguous:
+        raise ValueError("host index arrays must be C-contiguous numpy int32")
     return a.ctypes.data_as(_lib.P_i32)
 
 

@@ -87,7 +87,8 @@ def stage(w, seed: int = 0, batch: Optional[int] = None, lens: Optional[np.ndarr
 
     qidx_np, widx_np = synth.index_inputs(w, seed, H_I, B)
     q_np = synth.queries(w, seed, B)
-    assert q_np.shape[0] == B and qidx_np.shape[0] == B
+    if q_np.shape[0] != B or qidx_np.shape[0] != B:
+        raise ValueError(f"query sets hold {q_np.shape[0]} / {qidx_np.shape[0]} rows for {B} requests")
 
     table_dev = _dev(table, device)
     lens_dev = _dev(lens, device)
